@@ -1,0 +1,211 @@
+"""MI355X-native DSA (DeepSeek-style sparse attention) layer.
+
+A thin ctypes binding of libdsa.so (the gfx950 HIP kernels behind the C ABI
+declared in include/dsa.h). This module only marshals arguments: it reads
+shapes from torch tensors, allocates outputs and workspace with torch, and
+passes raw device pointers and the current HIP stream to the library. Every
+step of the layer runs in the library's kernels. There is no fallback: if the
+library is missing or a tensor is not on the GPU, calls raise.
+
+Entry points (same names as the C ABI, without the prefix):
+  index_scores, topk_mask, sparse_attention, forward, workspace_size
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # imported before libdsa.so so both resolve to one HIP runtime
+
+__all__ = [
+    "DsaError", "DSA_OP_INDEX_SCORES", "DSA_OP_TOPK_MASK", "DSA_OP_SPARSE_ATTENTION",
+    "DSA_OP_FORWARD", "library_path", "lib", "make_dims", "index_scores", "topk_mask",
+    "sparse_attention", "forward", "workspace_size", "lpad",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libdsa.so")
+
+DSA_FP32, DSA_BF16 = 0, 1
+DSA_OP_INDEX_SCORES, DSA_OP_TOPK_MASK, DSA_OP_SPARSE_ATTENTION, DSA_OP_FORWARD = 0, 1, 2, 3
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"dsa status {status}: {detail}")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("q_pos0", ctypes.c_int32),
+        ("n_kv", ctypes.c_int32), ("kv_capacity", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32), ("top_k", ctypes.c_int32), ("heads", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "dsa_index_scores": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P]),
+    "dsa_topk_mask": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "dsa_sparse_attention": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P,
+                                            ctypes.c_size_t, _P]),
+    "dsa_forward": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _P, ctypes.c_size_t, _P]),
+    "dsa_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
+    "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
+    "dsa_last_error": (ctypes.c_char_p, []),
+    "dsa_abi_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libdsa.so (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise ImportError(f"{library_path} is not built; run __graft_entry__.build()")
+        handle = ctypes.CDLL(library_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        detail = lib().dsa_last_error().decode()
+        raise DsaError(status, detail or lib().dsa_status_string(status).decode())
+
+
+def lpad(n_kv: int) -> int:
+    return (n_kv + 63) // 64 * 64
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float32:
+        return DSA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("DSA tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("DSA tensors must be contiguous")
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def make_dims(*, batch, n_q, q_pos0, n_kv, kv_capacity, idx_heads=1, idx_dim=32, top_k=1,
+              heads=1, kv_heads=1, head_dim=64, scale=None, dtype=DSA_BF16) -> Dims:
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return Dims(batch, n_q, q_pos0, n_kv, kv_capacity, idx_heads, idx_dim, top_k, heads,
+                kv_heads, head_dim, scale, dtype)
+
+
+def workspace_size(dims: Dims, op: int) -> int:
+    return int(lib().dsa_workspace_size(ctypes.byref(dims), op))
+
+
+def _workspace(dims: Dims, op: int, device, ws=None):
+    need = workspace_size(dims, op)
+    if need == 0:
+        return None, 0
+    if ws is not None:
+        if ws.numel() * ws.element_size() < need:
+            raise ValueError(f"workspace of {ws.numel() * ws.element_size()} bytes, need {need}")
+        return ws, ws.numel() * ws.element_size()
+    return torch.empty(need, dtype=torch.uint8, device=device), need
+
+
+def index_scores(qidx, w, kidx, *, q_pos0=0, n_kv=None, out=None):
+    """scores [B, T, Lpad] float32 of the lightning indexer; -inf for s > p."""
+    _need_gpu(qidx, w, kidx, out)
+    B, T, HI, DI = qidx.shape
+    cap = kidx.shape[1]
+    n_kv = cap if n_kv is None else n_kv
+    d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, idx_heads=HI,
+                  idx_dim=DI, dtype=_dtype_code(qidx))
+    if out is None:
+        out = torch.empty((B, T, lpad(n_kv)), dtype=torch.float32, device=qidx.device)
+    _check(lib().dsa_index_scores(ctypes.byref(d), _ptr(qidx), _ptr(w), _ptr(kidx), _ptr(out),
+                                  _stream(qidx)))
+    return out
+
+
+def topk_mask(scores, *, q_pos0=0, n_kv, top_k, indices=True):
+    """(mask [B, T, Lpad/32] int32 bit patterns, indices [B, T, top_k] int32 or None)."""
+    _need_gpu(scores)
+    B, T, L = scores.shape
+    d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=n_kv, top_k=top_k)
+    if L != lpad(n_kv):
+        raise ValueError(f"scores rows must have {lpad(n_kv)} entries")
+    mask = torch.empty((B, T, L // 32), dtype=torch.int32, device=scores.device)
+    idx = torch.empty((B, T, top_k), dtype=torch.int32, device=scores.device) if indices else None
+    _check(lib().dsa_topk_mask(ctypes.byref(d), _ptr(scores), _ptr(mask), _ptr(idx), None, 0,
+                               _stream(scores)))
+    return mask, idx
+
+
+def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=False, workspace=None):
+    """out [B, T, H, D] (and lse [B, T, H] float32) over the masked-in keys."""
+    _need_gpu(q, k, v, mask, workspace)
+    B, T, H, D = q.shape
+    cap, Hkv = k.shape[1], k.shape[2]
+    n_kv = cap if n_kv is None else n_kv
+    d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, heads=H,
+                  kv_heads=Hkv, head_dim=D, scale=scale, dtype=_dtype_code(q))
+    out = torch.empty_like(q)
+    lse_t = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if lse else None
+    ws, nbytes = _workspace(d, DSA_OP_SPARSE_ATTENTION, q.device, workspace)
+    _check(lib().dsa_sparse_attention(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
+                                      _ptr(out), _ptr(lse_t), _ptr(ws), nbytes, _stream(q)))
+    return (out, lse_t) if lse else out
+
+
+def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
+            return_indices=True, return_mask=False, return_lse=False, workspace=None, out=None):
+    """The whole DSA layer. Returns a dict with 'out' and the requested extras
+    ('indices' [B, T, top_k] int32, 'mask' [B, T, Lpad/32] int32, 'lse')."""
+    _need_gpu(qidx, w, kidx, q, k, v, workspace, out)
+    B, T, HI, DI = qidx.shape
+    H, D = q.shape[2], q.shape[3]
+    cap, Hkv = k.shape[1], k.shape[2]
+    n_kv = cap if n_kv is None else n_kv
+    d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, idx_heads=HI,
+                  idx_dim=DI, top_k=top_k, heads=H, kv_heads=Hkv, head_dim=D, scale=scale,
+                  dtype=_dtype_code(q))
+    dev = q.device
+    res = {"out": torch.empty_like(q) if out is None else out}
+    if return_indices:
+        res["indices"] = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
+    if return_mask:
+        res["mask"] = torch.empty((B, T, lpad(n_kv) // 32), dtype=torch.int32, device=dev)
+    if return_lse:
+        res["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    ws, nbytes = _workspace(d, DSA_OP_FORWARD, dev, workspace)
+    _check(lib().dsa_forward(ctypes.byref(d), _ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(res["out"]), _ptr(res.get("lse")),
+                             _ptr(res.get("indices")), _ptr(res.get("mask")), _ptr(ws), nbytes,
+                             _stream(q)))
+    return res

@@ -1,0 +1,74 @@
+"""Builds libdsa.so (gfx950 HIP kernels + the C ABI) in the package directory.
+
+    python -m dsa_lightning_indexer_03_amd.build
+
+Compiles every source with hipcc for gfx950 and links one shared library.
+Packed-fp32 instructions are disabled for all device code.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "dsa_api.cpp"]
+LIB_NAME = "libdsa.so"
+ARCH = "gfx950"
+
+
+def _hipcc() -> str:
+    cand = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(cand):
+        raise RuntimeError(f"hipcc not found (looked for {cand})")
+    return cand
+
+
+def common_flags() -> list[str]:
+    return [
+        "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
+    ]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int = 4) -> str:
+    """Compiles all sources and links libdsa.so; returns its path."""
+    hipcc = _hipcc()
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(obj_dir, src.replace(".", "_") + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmds.append([hipcc, *common_flags(), *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    out = os.path.join(HERE, LIB_NAME)
+    tmp = out + ".tmp"
+    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

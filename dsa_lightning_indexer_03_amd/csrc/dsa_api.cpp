@@ -1,0 +1,369 @@
+// C ABI of libdsa.so: argument validation (host only, before anything is
+// enqueued), workspace carving and kernel dispatch. See include/dsa.h.
+#include "dsa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "dsa_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dsa_status fail(dsa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dsa_status ok() {
+  g_last_error.clear();
+  return DSA_OK;
+}
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("DSA_DEBUG_SYNC");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+dsa_status hip_status(hipError_t e, const char* what, hipStream_t st) {
+  if (e == hipSuccess && debug_sync()) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return DSA_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t lpad_of(const dsa_dims& d) { return ((int64_t)d.n_kv + 63) / 64 * 64; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape rules shared by every op. `need_idx` / `need_attn` select which
+// dimension groups are checked.
+dsa_status check_dims(const dsa_dims* d, bool need_idx, bool need_attn, bool need_topk) {
+  if (!d) return fail(DSA_ERR_NULL, "dims is NULL");
+  if (d->batch < 1 || d->n_q < 1) return fail(DSA_ERR_SHAPE, "batch (%d) and n_q (%d) must be >= 1", d->batch, d->n_q);
+  if (d->q_pos0 < 0) return fail(DSA_ERR_SHAPE, "q_pos0 (%d) must be >= 0", d->q_pos0);
+  if (d->n_kv < 1 || (int64_t)d->q_pos0 + d->n_q > d->n_kv)
+    return fail(DSA_ERR_SHAPE, "need q_pos0 + n_q (%lld) <= n_kv (%d)", (long long)d->q_pos0 + d->n_q, d->n_kv);
+  if (d->kv_capacity < d->n_kv) return fail(DSA_ERR_SHAPE, "kv_capacity (%d) < n_kv (%d)", d->kv_capacity, d->n_kv);
+  if (d->dtype != DSA_FP32 && d->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
+  if (d->n_kv > dsa::kTopkMaxRow)
+    return fail(DSA_ERR_UNSUPPORTED, "n_kv %d above the supported maximum %d", d->n_kv, dsa::kTopkMaxRow);
+  if ((int64_t)d->batch * d->n_q > (1ll << 30)) return fail(DSA_ERR_SHAPE, "batch * n_q too large");
+  if (need_idx) {
+    if (d->idx_heads < 1 || d->idx_heads > 32)
+      return fail(d->idx_heads < 1 ? DSA_ERR_SHAPE : DSA_ERR_UNSUPPORTED, "idx_heads %d not in [1, 32]", d->idx_heads);
+    if (d->idx_dim != 32 && d->idx_dim != 64 && d->idx_dim != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "idx_dim %d not in {32, 64, 128}", d->idx_dim);
+    if (d->dtype == DSA_FP32 && d->idx_dim == 128)
+      return fail(DSA_ERR_UNSUPPORTED, "idx_dim 128 needs bf16 (fp32 supports 32 and 64)");
+  }
+  if (need_topk && d->top_k < 1) return fail(DSA_ERR_SHAPE, "top_k (%d) must be >= 1", d->top_k);
+  if (need_attn) {
+    if (d->heads < 1 || d->kv_heads < 1 || d->heads % d->kv_heads != 0)
+      return fail(DSA_ERR_SHAPE, "heads (%d) must be a positive multiple of kv_heads (%d)", d->heads, d->kv_heads);
+    if (d->head_dim != 64 && d->head_dim != 128)
+      return fail(DSA_ERR_UNSUPPORTED, "head_dim %d not in {64, 128}", d->head_dim);
+    if (!(d->scale > 0.f) || !std::isfinite(d->scale)) return fail(DSA_ERR_SHAPE, "scale must be finite and > 0");
+  }
+  return DSA_OK;
+}
+
+dsa_status check_ptr(const void* p, const char* name, bool required = true) {
+  if (!p) return required ? fail(DSA_ERR_NULL, "%s is NULL", name) : DSA_OK;
+  if (!aligned16(p)) return fail(DSA_ERR_MISALIGNED, "%s is not 16-byte aligned", name);
+  return DSA_OK;
+}
+
+#define DSA_TRY(x)                     \
+  do {                                 \
+    dsa_status s_ = (x);               \
+    if (s_ != DSA_OK) return s_;       \
+  } while (0)
+
+// The gather (decode) attention path runs for few queries per sequence.
+bool use_gather(const dsa_dims& d) { return d.n_q <= 8 && dsa::gather_supported(d.heads, d.head_dim); }
+
+int gather_splits(int64_t max_kept) { return (int)((max_kept + dsa::kGatherSplit - 1) / dsa::kGatherSplit); }
+
+// Workspace layouts. Every region starts 256-B aligned.
+struct AttnWs {
+  size_t list = 0, counts = 0, part_o = 0, part_ml = 0, total = 0;
+  int list_stride = 0, n_splits = 0;
+};
+AttnWs attn_ws(const dsa_dims& d, bool have_list) {
+  AttnWs w;
+  if (!use_gather(d)) return w;
+  const int64_t rows = (int64_t)d.batch * d.n_q;
+  const int64_t max_p1 = (int64_t)d.q_pos0 + d.n_q;
+  int64_t max_kept = max_p1;
+  size_t off = 0;
+  if (!have_list) {
+    w.list_stride = (int)max_p1;
+    w.list = off;
+    off += align_up((size_t)rows * w.list_stride * 4);
+    w.counts = off;
+    off += align_up((size_t)rows * 4);
+  } else {
+    max_kept = std::min<int64_t>(max_p1, d.top_k);
+  }
+  w.n_splits = gather_splits(max_kept);
+  w.part_o = off;
+  off += align_up((size_t)rows * w.n_splits * d.heads * d.head_dim * 4);
+  w.part_ml = off;
+  off += align_up((size_t)rows * w.n_splits * d.heads * 2 * 4);
+  w.total = off;
+  return w;
+}
+
+struct FwdWs {
+  size_t scores = 0, mask = 0, indices = 0, attn = 0, total = 0;
+  AttnWs aw;
+};
+FwdWs fwd_ws(const dsa_dims& d, bool user_mask, bool user_indices) {
+  FwdWs w;
+  const int64_t rows = (int64_t)d.batch * d.n_q;
+  const int64_t lp = lpad_of(d);
+  size_t off = 0;
+  w.scores = off;
+  off += align_up((size_t)rows * lp * 4);
+  if (!user_mask) {
+    w.mask = off;
+    off += align_up((size_t)rows * (lp / 32) * 4);
+  }
+  const bool gather = use_gather(d);
+  if (gather && !user_indices) {
+    w.indices = off;
+    off += align_up((size_t)rows * d.top_k * 4);
+  }
+  w.aw = attn_ws(d, /*have_list=*/true);
+  w.attn = off;
+  off += w.aw.total;
+  w.total = off;
+  return w;
+}
+
+dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const void* kidx, float* scores,
+                      bool write_upper, hipStream_t st) {
+  dsa::IndexerParams p{};
+  p.qidx = qidx;
+  p.w = w;
+  p.kidx = kidx;
+  p.scores = scores;
+  p.B = d.batch;
+  p.T = d.n_q;
+  p.q_pos0 = d.q_pos0;
+  p.n_kv = d.n_kv;
+  p.kv_cap = d.kv_capacity;
+  p.HI = d.idx_heads;
+  p.Lpad = (int)lpad_of(d);
+  p.write_upper = write_upper ? 1 : 0;
+  return hip_status(dsa::launch_indexer(p, d.dtype, d.idx_dim, st), "indexer launch", st);
+}
+
+dsa_status run_topk(const dsa_dims& d, const float* scores, uint32_t* mask, int32_t* indices, hipStream_t st) {
+  dsa::TopkParams p{};
+  p.scores = scores;
+  p.mask = mask;
+  p.indices = indices;
+  p.B = d.batch;
+  p.T = d.n_q;
+  p.q_pos0 = d.q_pos0;
+  p.n_kv = d.n_kv;
+  p.Lpad = (int)lpad_of(d);
+  p.top_k = d.top_k;
+  return hip_status(dsa::launch_topk(p, st), "top-k launch", st);
+}
+
+dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const void* v, const uint32_t* mask,
+                         const int32_t* list, void* out, float* lse, unsigned char* ws, const AttnWs& aw,
+                         hipStream_t st) {
+  const float scale_log2 = d.scale * 1.4426950408889634f;
+  if (!use_gather(d)) {
+    dsa::AttnParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.mask = mask;
+    p.out = out;
+    p.lse = lse;
+    p.B = d.batch;
+    p.T = d.n_q;
+    p.q_pos0 = d.q_pos0;
+    p.n_kv = d.n_kv;
+    p.kv_cap = d.kv_capacity;
+    p.H = d.heads;
+    p.Hkv = d.kv_heads;
+    p.Lpad = (int)lpad_of(d);
+    p.scale_log2 = scale_log2;
+    return hip_status(dsa::launch_attn_prefill(p, d.dtype, d.head_dim, st), "attention launch", st);
+  }
+  dsa::GatherParams g{};
+  g.q = q;
+  g.k = k;
+  g.v = v;
+  if (list) {
+    g.list = list;
+    g.counts = nullptr;
+    g.list_stride = d.top_k;
+  } else {
+    dsa::CompactParams cp{};
+    cp.mask = mask;
+    cp.list = reinterpret_cast<int32_t*>(ws + aw.list);
+    cp.counts = reinterpret_cast<int32_t*>(ws + aw.counts);
+    cp.B = d.batch;
+    cp.T = d.n_q;
+    cp.q_pos0 = d.q_pos0;
+    cp.n_kv = d.n_kv;
+    cp.Lpad = (int)lpad_of(d);
+    cp.list_stride = aw.list_stride;
+    DSA_TRY(hip_status(dsa::launch_mask_compact(cp, st), "mask compaction launch", st));
+    g.list = cp.list;
+    g.counts = cp.counts;
+    g.list_stride = aw.list_stride;
+  }
+  g.top_k = d.top_k;
+  g.part_o = reinterpret_cast<float*>(ws + aw.part_o);
+  g.part_ml = reinterpret_cast<float*>(ws + aw.part_ml);
+  g.out = out;
+  g.lse = lse;
+  g.B = d.batch;
+  g.T = d.n_q;
+  g.q_pos0 = d.q_pos0;
+  g.n_kv = d.n_kv;
+  g.kv_cap = d.kv_capacity;
+  g.H = d.heads;
+  g.Hkv = d.kv_heads;
+  g.n_splits = aw.n_splits;
+  g.scale_log2 = scale_log2;
+  return hip_status(dsa::launch_attn_gather(g, d.dtype, d.head_dim, st), "gather attention launch", st);
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_index_scores(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
+                            float* scores, void* stream) {
+  DSA_TRY(check_dims(dims, true, false, false));
+  DSA_TRY(check_ptr(qidx, "qidx"));
+  DSA_TRY(check_ptr(w, "w"));
+  DSA_TRY(check_ptr(kidx, "kidx"));
+  DSA_TRY(check_ptr(scores, "scores"));
+  DSA_TRY(run_scores(*dims, qidx, w, kidx, scores, true, (hipStream_t)stream));
+  return ok();
+}
+
+dsa_status dsa_topk_mask(const dsa_dims* dims, const float* scores, uint32_t* mask, int32_t* indices, void* ws,
+                         size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  DSA_TRY(check_dims(dims, false, false, true));
+  DSA_TRY(check_ptr(scores, "scores"));
+  DSA_TRY(check_ptr(mask, "mask"));
+  DSA_TRY(check_ptr(indices, "indices", false));
+  DSA_TRY(run_topk(*dims, scores, mask, indices, (hipStream_t)stream));
+  return ok();
+}
+
+dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void* k_cache, const void* v_cache,
+                                const uint32_t* mask, void* out, float* lse, void* ws, size_t ws_bytes,
+                                void* stream) {
+  DSA_TRY(check_dims(dims, false, true, false));
+  DSA_TRY(check_ptr(q, "q"));
+  DSA_TRY(check_ptr(k_cache, "k_cache"));
+  DSA_TRY(check_ptr(v_cache, "v_cache"));
+  DSA_TRY(check_ptr(mask, "mask"));
+  DSA_TRY(check_ptr(out, "out"));
+  DSA_TRY(check_ptr(lse, "lse", false));
+  const AttnWs aw = attn_ws(*dims, false);
+  if (aw.total > 0) {
+    DSA_TRY(check_ptr(ws, "workspace"));
+    if (ws_bytes < aw.total)
+      return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, aw.total);
+  }
+  DSA_TRY(run_attention(*dims, q, k_cache, v_cache, mask, nullptr, out, lse, (unsigned char*)ws, aw,
+                        (hipStream_t)stream));
+  return ok();
+}
+
+dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx, const void* q,
+                       const void* k_cache, const void* v_cache, void* out, float* lse, int32_t* indices,
+                       uint32_t* mask, void* ws, size_t ws_bytes, void* stream) {
+  DSA_TRY(check_dims(dims, true, true, true));
+  DSA_TRY(check_ptr(qidx, "qidx"));
+  DSA_TRY(check_ptr(w, "w"));
+  DSA_TRY(check_ptr(kidx, "kidx"));
+  DSA_TRY(check_ptr(q, "q"));
+  DSA_TRY(check_ptr(k_cache, "k_cache"));
+  DSA_TRY(check_ptr(v_cache, "v_cache"));
+  DSA_TRY(check_ptr(out, "out"));
+  DSA_TRY(check_ptr(lse, "lse", false));
+  DSA_TRY(check_ptr(indices, "indices", false));
+  DSA_TRY(check_ptr(mask, "mask", false));
+  const dsa_dims& d = *dims;
+  const FwdWs fw = fwd_ws(d, mask != nullptr, indices != nullptr);
+  DSA_TRY(check_ptr(ws, "workspace"));
+  if (ws_bytes < fw.total) return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, fw.total);
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* wsb = (unsigned char*)ws;
+  float* scores = reinterpret_cast<float*>(wsb + fw.scores);
+  uint32_t* m = mask ? mask : reinterpret_cast<uint32_t*>(wsb + fw.mask);
+  const bool gather = use_gather(d);
+  int32_t* idx = indices ? indices : (gather ? reinterpret_cast<int32_t*>(wsb + fw.indices) : nullptr);
+  DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
+  DSA_TRY(run_topk(d, scores, m, idx, st));
+  DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw, st));
+  return ok();
+}
+
+size_t dsa_workspace_size(const dsa_dims* dims, int32_t op) {
+  if (!dims) return 0;
+  const dsa_dims& d = *dims;
+  switch (op) {
+    case DSA_OP_INDEX_SCORES:
+    case DSA_OP_TOPK_MASK:
+      return 0;
+    case DSA_OP_SPARSE_ATTENTION:
+      if (check_dims(dims, false, true, false) != DSA_OK) return 0;
+      return attn_ws(d, false).total;
+    case DSA_OP_FORWARD:
+      if (check_dims(dims, true, true, true) != DSA_OK) return 0;
+      return fwd_ws(d, false, false).total;
+    default:
+      return 0;
+  }
+}
+
+const char* dsa_status_string(int32_t status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "null pointer";
+    case DSA_ERR_SHAPE: return "invalid shape";
+    case DSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DSA_ERR_MISALIGNED: return "misaligned pointer";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dsa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+}  // extern "C"

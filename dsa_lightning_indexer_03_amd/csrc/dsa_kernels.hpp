@@ -1,0 +1,75 @@
+// Host-side launchers of the gfx950 DSA kernels (internal to libdsa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Lightning-indexer scores for T queries of B sequences.
+struct IndexerParams {
+  const void* qidx;   // [B][T][HI][DI]
+  const float* w;     // [B][T][HI]
+  const void* kidx;   // [B][kv_cap][DI]
+  float* scores;      // [B][T][Lpad]
+  int B, T, q_pos0, n_kv, kv_cap, HI, Lpad;
+  int key_chunk;      // keys per workgroup (multiple of 64)
+  int write_upper;    // 1: write -inf for s > p; 0: leave those entries untouched
+};
+hipError_t launch_indexer(const IndexerParams& p, int dtype, int DI, hipStream_t st);
+
+// Top-k -> bitmask (+ ascending indices).
+struct TopkParams {
+  const float* scores;  // [B][T][Lpad]
+  uint32_t* mask;       // [B][T][Lpad/32]
+  int32_t* indices;     // [B][T][top_k] or nullptr
+  int B, T, q_pos0, n_kv, Lpad, top_k;
+};
+hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+
+// Masked flash attention over 64-key tiles (prefill-shaped calls).
+struct AttnParams {
+  const void* q;         // [B][T][H][D]
+  const void* k;         // [B][kv_cap][Hkv][D]
+  const void* v;
+  const uint32_t* mask;  // [B][T][Lpad/32]
+  void* out;             // [B][T][H][D]
+  float* lse;            // [B][T][H] or nullptr
+  int B, T, q_pos0, n_kv, kv_cap, H, Hkv, Lpad;
+  float scale_log2;      // softmax scale * log2(e)
+};
+hipError_t launch_attn_prefill(const AttnParams& p, int dtype, int D, hipStream_t st);
+
+// Gather attention for few queries per sequence: kept-token lists -> split
+// partials -> combine.
+struct GatherParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* list;    // [B*T][list_stride] ascending kept tokens
+  const int32_t* counts;  // [B*T] kept-token counts, or nullptr: min(top_k, p+1)
+  int list_stride, top_k;
+  float* part_o;          // [B*T][n_splits][H][D] float
+  float* part_ml;         // [B*T][n_splits][H][2] float (max in log2 units, sum)
+  void* out;              // [B][T][H][D]
+  float* lse;             // [B][T][H] or nullptr
+  int B, T, q_pos0, n_kv, kv_cap, H, Hkv, n_splits;
+  float scale_log2;
+};
+constexpr int kGatherSplit = 128;  // kept tokens per split workgroup
+bool gather_supported(int H, int D);
+hipError_t launch_attn_gather(const GatherParams& p, int dtype, int D, hipStream_t st);
+
+// Compacts mask rows (bits s <= p, s < n_kv) into ascending token lists.
+struct CompactParams {
+  const uint32_t* mask;  // [B][T][Lpad/32]
+  int32_t* list;         // [B*T][list_stride]
+  int32_t* counts;       // [B*T]
+  int B, T, q_pos0, n_kv, Lpad, list_stride;
+};
+hipError_t launch_mask_compact(const CompactParams& p, hipStream_t st);
+
+// Largest row length (p + 1) the top-k kernel holds in registers.
+constexpr int kTopkMaxRow = 65536;
+
+}  // namespace dsa

@@ -1,0 +1,164 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DSA layer library, libdsa.so.
+ *
+ * One DSA (DeepSeek-style sparse attention) layer: a lightning indexer scores
+ * every earlier cached token for each query, each query keeps its top_k
+ * best-scored tokens, the selection is applied as a bitmask over the whole
+ * cache, and attention runs only over the kept keys.
+ *
+ * Pages this interface follows (text of three news pages on llama.cpp build
+ * b12180 and the Kimi-K3.1-Pro model):
+ *   [aiaulis] aiaulis.com, "llama.cpp kan nu köra Kimi-K3.1-Pro, men än så
+ *             länge bara text", paragraphs 2-4 and 7.
+ *   [aiu]     aiunderstanding.org, "llama.cpp adds support for Kimi-K3.1-Pro
+ *             architecture with DSA indexer", section "What happened".
+ *   [devotd]  devotd.net, "llama.cpp b12180 Kimi-K3.1-Pro", sections 1, 2, 4
+ *             and the indexer-configuration table of section 1.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE memory allocated and owned by the caller.
+ *    The library allocates nothing and keeps no state between calls besides a
+ *    thread-local error string. Calls are reentrant.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    call only enqueues kernels on it and returns; results are ready once the
+ *    caller synchronises the stream.
+ *  - Validation is done on the host before anything is enqueued. A call that
+ *    returns an error status has enqueued nothing and written no output.
+ *    DSA_ERR_HIP means a launch failed; a fault during execution surfaces at
+ *    the caller's next synchronisation.
+ *  - All pointers must be 16-byte aligned (DSA_ERR_MISALIGNED otherwise).
+ *  - Inputs must be finite. Non-finite inputs are not detected.
+ *  - Query i of a sequence sits at absolute position p = q_pos0 + i. Its
+ *    candidates are the cached tokens s = 0..p (causal, itself included).
+ *  - Lpad = roundup(n_kv, 64): the row length of score rows, and 32 times the
+ *    number of 32-bit words in a mask row.
+ *
+ * Tensor layouts (row-major, batch outermost, T = n_q, L = kv_capacity):
+ *   qidx    [B][T][idx_heads][idx_dim]   indexer queries, dtype
+ *   w       [B][T][idx_heads]            indexer head weights, float32
+ *   kidx    [B][L][idx_dim]              indexer-key cache, dtype
+ *   scores  [B][T][Lpad]                 float32
+ *   mask    [B][T][Lpad/32]              uint32; token s is kept when bit
+ *                                        (s & 31) of word (s >> 5) is set
+ *   indices [B][T][top_k]                int32, ascending, -1 padded
+ *   q, out  [B][T][heads][head_dim]      dtype
+ *   k, v    [B][L][kv_heads][head_dim]   attention key/value caches, dtype
+ *   lse     [B][T][heads]                float32, natural-log sum-exp
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer (or dims) is NULL          */
+  DSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range            */
+  DSA_ERR_UNSUPPORTED = 3, /* valid request this build has no kernel for    */
+  DSA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned              */
+  DSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required       */
+  DSA_ERR_HIP = 6          /* the HIP runtime rejected a launch             */
+} dsa_status;
+
+typedef enum { DSA_FP32 = 0, DSA_BF16 = 1 } dsa_dtype;
+
+typedef enum {
+  DSA_OP_INDEX_SCORES = 0,
+  DSA_OP_TOPK_MASK = 1,
+  DSA_OP_SPARSE_ATTENTION = 2,
+  DSA_OP_FORWARD = 3
+} dsa_op;
+
+/* Problem sizes of one call.
+ * Supported: dtype in {DSA_FP32, DSA_BF16}; idx_dim in {32, 64, 128} for bf16
+ * and {32, 64} for fp32;
+ * head_dim in {64, 128}; 1 <= idx_heads <= 32; heads % kv_heads == 0;
+ * n_kv <= 65536 and q_pos0 + n_q <= n_kv <= kv_capacity; top_k >= 1.
+ * The configuration of the pages is idx_heads 32, idx_dim 128, top_k 2048
+ * [aiu "What happened"; devotd section 1 table]. */
+typedef struct {
+  int32_t batch;       /* B: independent sequences                          */
+  int32_t n_q;         /* T: queries per sequence in this call              */
+  int32_t q_pos0;      /* absolute position of query 0                      */
+  int32_t n_kv;        /* cached tokens 0..n_kv-1 that may be read          */
+  int32_t kv_capacity; /* L: token capacity of the caches (batch stride)    */
+  int32_t idx_heads;   /* H_I: indexer heads                                */
+  int32_t idx_dim;     /* D_I: indexer query/key dim                        */
+  int32_t top_k;       /* tokens kept per query                             */
+  int32_t heads;       /* H: attention query heads                          */
+  int32_t kv_heads;    /* H_kv: key/value heads (heads % kv_heads == 0)     */
+  int32_t head_dim;    /* D: attention head dim                             */
+  float scale;         /* softmax scale, > 0 (usually 1/sqrt(head_dim))     */
+  int32_t dtype;       /* dsa_dtype of qidx, kidx, q, k, v, out             */
+} dsa_dims;
+
+/* Lightning-indexer scores [aiaulis para 2; aiu "What happened"; devotd
+ * sections 1-2]. The pages give no formula; the reading implemented is
+ *   scores[b][i][s] = sum_h w[b][i][h] * max(0, sum_d qidx[b][i][h][d] * kidx[b][s][d])
+ * for s <= p, accumulated in float32 (bf16 products are exact in float32);
+ * no RoPE, no scale. Entries s > p (and s >= n_kv) are written as -inf.
+ * Reads qidx, w, kidx[b][0..n_kv-1]; writes scores. No workspace. */
+dsa_status dsa_index_scores(const dsa_dims* dims, const void* qidx, const float* w,
+                            const void* kidx, float* scores, void* stream);
+
+/* Top-k selection applied as a mask over the whole cache [aiaulis paras 3-4;
+ * devotd sections 1-2]. Per query row: if top_k >= p+1 every candidate
+ * 0..p is kept; otherwise the top_k largest scores among s = 0..p, ties going
+ * to the lower index (-0.0 equals +0.0). Writes mask (bits of tokens not kept,
+ * s > p and s >= n_kv are zero) and, when `indices` is not NULL, the kept
+ * indices ascending, padded with -1 to top_k. Reads scores[b][i][0..p] only.
+ * `ws` may be NULL when dsa_workspace_size(dims, DSA_OP_TOPK_MASK) is 0. */
+dsa_status dsa_topk_mask(const dsa_dims* dims, const float* scores, uint32_t* mask,
+                         int32_t* indices, void* ws, size_t ws_bytes, void* stream);
+
+/* Attention over the kept keys only [aiaulis paras 2 and 4; devotd section
+ * 2]: for each query i and head h, over the keys S_i = {s <= p, s < n_kv,
+ * mask bit s set},
+ *   out[b][i][h] = sum_{s in S_i} softmax_s(scale * q[b][i][h] . k[b][s][g]) v[b][s][g],
+ * g = h / (heads / kv_heads). Keys outside S_i get exactly zero weight. An
+ * empty S_i gives out = 0 and lse = -inf. lse (optional, may be NULL) is the
+ * natural-log sum-exp of the scaled scores over S_i.
+ * Prefill-shaped calls run a masked flash attention over 64-key tiles; calls
+ * with few queries per sequence gather the kept rows instead. Both compute
+ * the same function. Needs dsa_workspace_size(dims, DSA_OP_SPARSE_ATTENTION)
+ * bytes of workspace. */
+dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void* k_cache,
+                                const void* v_cache, const uint32_t* mask, void* out,
+                                float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: dsa_index_scores -> dsa_topk_mask -> dsa_sparse_attention
+ * with the scores kept in the workspace [aiaulis paras 2-4; devotd sections
+ * 1-2]. `indices`, `mask` and `lse` are optional outputs (NULL = not
+ * written; the mask then lives in the workspace). Needs
+ * dsa_workspace_size(dims, DSA_OP_FORWARD) bytes of workspace. */
+dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w,
+                       const void* kidx, const void* q, const void* k_cache,
+                       const void* v_cache, void* out, float* lse, int32_t* indices,
+                       uint32_t* mask, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes `op` needs for `dims` (0 when none). Returns 0 for invalid
+ * dims as well; the op itself then reports the error. Host only. */
+size_t dsa_workspace_size(const dsa_dims* dims, int32_t op);
+
+/* Static description of a status code. Host only. */
+const char* dsa_status_string(int32_t status);
+
+/* Detail of the last failing call on this thread ("" if none). Host only. */
+const char* dsa_last_error(void);
+
+/* DSA_ABI_VERSION of the built library. Host only. */
+int32_t dsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

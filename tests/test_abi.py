@@ -1,0 +1,135 @@
+"""Host-side checks of the C-ABI library that need no GPU: it loads, exports
+every entry point include/dsa.h declares, and rejects invalid arguments on the
+host before anything is enqueued. Every call here fails validation, so no
+kernel is ever launched. Pointers passed are fake, aligned addresses that the
+library never dereferences on these paths."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dsa_lightning_indexer_03_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_MISALIGNED, ERR_WORKSPACE, ERR_HIP = range(7)
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dsa.lib()
+    names = _declared_functions()
+    assert {"dsa_index_scores", "dsa_topk_mask", "dsa_sparse_attention", "dsa_forward"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.dsa_abi_version() == 1
+    assert lib.dsa_status_string(ERR_WORKSPACE) == b"workspace too small"
+
+
+def _dims(**kw):
+    base = dict(batch=1, n_q=16, q_pos0=0, n_kv=64, kv_capacity=64, idx_heads=32, idx_dim=128,
+                top_k=8, heads=32, kv_heads=32, head_dim=128, scale=None, dtype=dsa.DSA_BF16)
+    base.update(kw)
+    return dsa.make_dims(**base)
+
+
+def _scores(d, qidx=FAKE, w=FAKE, kidx=FAKE, scores=FAKE):
+    return dsa.lib().dsa_index_scores(ctypes.byref(d) if d is not None else None, qidx, w, kidx, scores, None)
+
+
+def _forward(d, ws=FAKE, ws_bytes=1 << 40, out=FAKE, idx=None, mask=None):
+    return dsa.lib().dsa_forward(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, out, None, idx, mask,
+                                 ws, ws_bytes, None)
+
+
+def _err():
+    return dsa.lib().dsa_last_error().decode()
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(n_q=0), ERR_SHAPE),
+        (dict(batch=0), ERR_SHAPE),
+        (dict(q_pos0=-1), ERR_SHAPE),
+        (dict(q_pos0=60, n_q=16), ERR_SHAPE),          # q_pos0 + n_q > n_kv
+        (dict(kv_capacity=32), ERR_SHAPE),              # capacity < n_kv
+        (dict(idx_heads=0), ERR_SHAPE),
+        (dict(idx_heads=33), ERR_UNSUPPORTED),
+        (dict(idx_dim=96), ERR_UNSUPPORTED),
+        (dict(idx_dim=128, dtype=dsa.DSA_FP32), ERR_UNSUPPORTED),
+        (dict(dtype=7), ERR_UNSUPPORTED),
+        (dict(n_kv=65600, kv_capacity=65600), ERR_UNSUPPORTED),
+    ],
+)
+def test_index_scores_rejects_bad_dims(kw, status):
+    assert _scores(_dims(**kw)) == status
+    assert _err() != ""
+
+
+def test_null_and_misaligned_pointers_are_rejected():
+    assert _scores(None) == ERR_NULL
+    assert _scores(_dims(), qidx=None) == ERR_NULL
+    assert _scores(_dims(), scores=None) == ERR_NULL
+    assert _scores(_dims(), w=FAKE + 4) == ERR_MISALIGNED
+    assert "w" in _err()
+
+
+def test_attention_and_forward_validation():
+    lib = dsa.lib()
+    d = _dims(head_dim=96)
+    assert lib.dsa_sparse_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_UNSUPPORTED
+    d = _dims(heads=30, kv_heads=4)
+    assert lib.dsa_sparse_attention(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == ERR_SHAPE
+    d = _dims(scale=-1.0)
+    assert _forward(d) == ERR_SHAPE
+    d = _dims(top_k=0)
+    assert _forward(d) == ERR_SHAPE
+    d = _dims()
+    assert _forward(d, out=None) == ERR_NULL
+    need = dsa.workspace_size(d, dsa.DSA_OP_FORWARD)
+    assert need > 0
+    assert _forward(d, ws=None) == ERR_NULL
+    assert _forward(d, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert "need" in _err()
+
+
+def test_topk_validation():
+    lib = dsa.lib()
+    d = _dims(top_k=0)
+    assert lib.dsa_topk_mask(ctypes.byref(d), FAKE, FAKE, None, None, 0, None) == ERR_SHAPE
+    d = _dims()
+    assert lib.dsa_topk_mask(ctypes.byref(d), FAKE, None, None, None, 0, None) == ERR_NULL
+    assert lib.dsa_topk_mask(ctypes.byref(d), FAKE, FAKE, FAKE + 8, None, 0, None) == ERR_MISALIGNED
+
+
+def test_workspace_sizes():
+    # prefill-shaped forward: scores [B, T, Lpad] + mask, each 256-B aligned
+    d = _dims(n_q=64, n_kv=100, kv_capacity=128)
+    lp = 128
+    want = (64 * lp * 4 + 255) // 256 * 256 + (64 * lp // 8 + 255) // 256 * 256
+    assert dsa.workspace_size(d, dsa.DSA_OP_FORWARD) == want
+    assert dsa.workspace_size(d, dsa.DSA_OP_SPARSE_ATTENTION) == 0
+    assert dsa.workspace_size(d, dsa.DSA_OP_INDEX_SCORES) == 0
+    # decode-shaped calls gather kept rows and need split partials
+    d = _dims(batch=4, n_q=1, q_pos0=999, n_kv=1000, kv_capacity=1000, top_k=300)
+    assert dsa.workspace_size(d, dsa.DSA_OP_SPARSE_ATTENTION) > 0
+    assert dsa.workspace_size(_dims(n_q=0), dsa.DSA_OP_FORWARD) == 0
+
+
+def test_binding_refuses_host_tensors():
+    """No CPU fallback: the binding raises instead of computing on the host."""
+    q = torch.zeros(1, 4, 32, 128, dtype=torch.bfloat16)
+    w = torch.zeros(1, 4, 32)
+    k = torch.zeros(1, 64, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dsa.index_scores(q, w, k)

@@ -1,0 +1,322 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Workload configurations at full size, plus edge cases
+(ragged sizes, batches, grouped heads, decode shapes, crafted ties)."""
+import math
+import sys
+import time
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_lightning_indexer_03_amd as dsa
+from dsa_workloads import WORKLOADS, Workload, make_inputs, sample_rows
+from oracle import full_causal_attention, pack_mask, round_scores_fp32, select_topk
+from tests.dsa_check import OUT_TOL, RowChecker, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    _say(f"\n[gpu-test] {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+
+
+def _np64(t):
+    return to_np(t).astype(np.float64)
+
+
+def _forward(inp, wl_like, top_k, q_pos0, n_kv, **kw):
+    return dsa.forward(inp["qidx"], inp["w"], inp["kidx"], inp["q"], inp["k"], inp["v"], top_k=top_k,
+                       q_pos0=q_pos0, n_kv=n_kv, scale=wl_like.scale, **kw)
+
+
+def _to(inp, dev):
+    return {k: v.to(dev) for k, v in inp.items()}
+
+
+def _check_sequence(wl, cpu, gpu_res, gpu_scores, b, rows, integer=False):
+    chk = RowChecker(wl.dtype, _np64(cpu["qidx"][b]), _np64(cpu["w"][b]), _np64(cpu["kidx"][b]),
+                     _np64(cpu["q"][b]), _np64(cpu["k"][b]), _np64(cpu["v"][b]), wl.q_pos0, wl.top_k,
+                     wl.scale, integer=integer)
+    sc = to_np(gpu_scores[b]) if gpu_scores is not None else None
+    idx = to_np(gpu_res["indices"][b])
+    out = to_np(gpu_res["out"][b])
+    lse = to_np(gpu_res["lse"][b]) if "lse" in gpu_res else None
+    for i in rows:
+        chk.check(i, None if sc is None else sc[i], idx[i], out[i], None if lse is None else lse[i])
+    return chk.stats
+
+
+# ------------------------------------------------------------------ workload configurations
+
+def test_tiny_fp32_L256_all_rows():
+    wl = WORKLOADS["tiny_fp32_L256"]
+    cpu = make_inputs(wl, "cpu")
+    g = _to(cpu, DEV)
+    res = _forward(g, wl, wl.top_k, wl.q_pos0, wl.n_kv, return_lse=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=0, n_kv=wl.n_kv)
+    torch.cuda.synchronize()
+    st = _check_sequence(wl, cpu, res, sc, 0, range(wl.n_q))
+    _say(f"stats {st}")
+
+
+def test_equiv_bf16_L1536_equals_full_causal_attention():
+    """top_k 2048 >= L: the layer must equal full causal attention [aiaulis
+    para 7; devotd section 4]; every row keeps its whole prefix."""
+    wl = WORKLOADS["equiv_bf16_L1536_k2048"]
+    cpu = make_inputs(wl, "cpu")
+    g = _to(cpu, DEV)
+    res = _forward(g, wl, wl.top_k, 0, wl.n_kv)
+    torch.cuda.synchronize()
+    idx = to_np(res["indices"][0])
+    for i in range(wl.n_q):
+        assert np.array_equal(idx[i, : i + 1], np.arange(i + 1)) and np.all(idx[i, i + 1 :] == -1)
+    full = full_causal_attention(_np64(cpu["q"][0]), _np64(cpu["k"][0]), _np64(cpu["v"][0]), 0, wl.scale)
+    err = np.abs(to_np(res["out"][0]).astype(np.float64) - full).max()
+    _say(f"max |out - full attention| = {err:.3e}")
+    assert err <= OUT_TOL["bf16"]
+
+
+def test_ties_bf16_L1536_bit_exact_selection():
+    """Integer indexer inputs: scores exact in fp32, many ties; scores and
+    kept sets must be bit-exact; below the context the output differs from
+    full attention [aiaulis para 7; devotd section 4]."""
+    wl = WORKLOADS["ties_bf16_L1536_k512"]
+    cpu = make_inputs(wl, "cpu")
+    g = _to(cpu, DEV)
+    res = _forward(g, wl, wl.top_k, 0, wl.n_kv, return_mask=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=0, n_kv=wl.n_kv)
+    torch.cuda.synchronize()
+    st = _check_sequence(wl, cpu, res, sc, 0, range(wl.n_q), integer=True)
+    # masks are the packed kept sets, bit for bit
+    mask = to_np(res["mask"][0]).view(np.uint32)
+    idx = to_np(res["indices"][0])
+    for i in range(0, wl.n_q, 97):
+        assert np.array_equal(mask[i], pack_mask(idx[i][idx[i] >= 0], wl.n_kv))
+    full = full_causal_attention(_np64(cpu["q"][0]), _np64(cpu["k"][0]), _np64(cpu["v"][0]), 0, wl.scale)
+    diff = np.abs(to_np(res["out"][0]).astype(np.float64) - full).max(axis=(1, 2))
+    assert np.all(diff[:512] <= OUT_TOL["bf16"])
+    assert np.all(diff[1024:] > OUT_TOL["bf16"])  # half the prefix dropped: clearly different
+    _say(f"stats {st}")
+
+
+def test_prefill_bf16_L4096_all_rows():
+    wl = WORKLOADS["prefill_bf16_L4096"]
+    cpu = make_inputs(wl, "cpu")
+    g = _to(cpu, DEV)
+    res = _forward(g, wl, wl.top_k, 0, wl.n_kv, return_lse=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=0, n_kv=wl.n_kv)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    st = _check_sequence(wl, cpu, res, sc, 0, range(wl.n_q))
+    _say(f"stats {st} oracle {time.time() - t0:.1f}s")
+
+
+def test_decode_bf16_B64_L32768_all_rows():
+    wl = WORKLOADS["decode_bf16_B64_L32768"]
+    g = make_inputs(wl, DEV)
+    res = _forward(g, wl, wl.top_k, wl.q_pos0, wl.n_kv, return_lse=True)
+    torch.cuda.synchronize()
+    idx_all = to_np(res["indices"])
+    out_all = to_np(res["out"])
+    lse_all = to_np(res["lse"])
+    total = {"sel_diff_rows": 0, "max_out_err": 0.0}
+    for b in range(wl.batch):
+        kc_dev, vc_dev = g["k"][b], g["v"][b]
+
+        def rows_of(cache):
+            return lambda sel: _np64(cache[torch.as_tensor(np.asarray(sel), device=DEV, dtype=torch.long)])
+
+        chk = RowChecker(wl.dtype, _np64(g["qidx"][b]), _np64(g["w"][b]), _np64(g["kidx"][b, : wl.n_kv]),
+                         _np64(g["q"][b]), rows_of(kc_dev), rows_of(vc_dev), wl.q_pos0, wl.top_k, wl.scale)
+        chk.check(0, None, idx_all[b, 0], out_all[b, 0], lse_all[b, 0])
+        total["sel_diff_rows"] += chk.stats["sel_diff_rows"]
+        total["max_out_err"] = max(total["max_out_err"], chk.stats["max_out_err"])
+    _say(f"stats {total}")
+
+
+def test_longctx_bf16_L65536_chunked_sampled_rows():
+    wl = WORKLOADS["longctx_bf16_L65536_chunk4096"]
+    g = make_inputs(wl, DEV)
+    C = wl.chunk_len
+    out = torch.empty_like(g["q"])
+    idx = torch.empty((1, wl.n_q, wl.top_k), dtype=torch.int32, device=DEV)
+    for c in range(wl.chunks):
+        sl = slice(c * C, (c + 1) * C)
+        r = dsa.forward(g["qidx"][:, sl], g["w"][:, sl], g["kidx"], g["q"][:, sl], g["k"], g["v"],
+                        top_k=wl.top_k, q_pos0=c * C, n_kv=(c + 1) * C, scale=wl.scale)
+        out[:, sl] = r["out"]
+        idx[:, sl] = r["indices"]
+    torch.cuda.synchronize()
+    rows = sample_rows(wl, 512)
+    rsel = torch.as_tensor(rows, device=DEV)
+    kc = to_np(g["k"][0])  # host copies of the caches (bf16 values as float32)
+    vc = to_np(g["v"][0])
+    chk = RowChecker(wl.dtype, None, None, _np64(g["kidx"][0]), None, kc, vc, 0, wl.top_k, wl.scale)
+    qidx_r = _np64(g["qidx"][0, rsel])
+    w_r = _np64(g["w"][0, rsel])
+    q_r = _np64(g["q"][0, rsel])
+    idx_r = to_np(idx[0, rsel])
+    out_r = to_np(out[0, rsel])
+    t0 = time.time()
+    for j, i in enumerate(rows):
+        chk.qidx = qidx_r[j : j + 1]
+        chk.w = w_r[j : j + 1]
+        chk.q = q_r[j : j + 1]
+        chk.q_pos0 = i
+        chk.check(0, None, idx_r[j], out_r[j])
+    _say(f"stats {chk.stats} oracle {time.time() - t0:.1f}s")
+
+
+# ------------------------------------------------------------------ edge cases
+
+EDGE = [
+    # name, dtype, B, T, q_pos0, n_kv, cap, HI, DI, k, H, Hkv, D, integer
+    ("ragged_gqa_batch", "bf16", 2, 100, 37, 150, 160, 32, 128, 50, 8, 2, 128, False),
+    ("topk1_small_heads", "bf16", 1, 200, 0, 200, 200, 12, 64, 1, 4, 4, 64, False),
+    ("fp32_keep_all_gqa", "fp32", 1, 70, 10, 90, 90, 20, 32, 300, 4, 1, 128, False),
+    ("fp32_idx64", "fp32", 1, 130, 0, 130, 130, 32, 64, 17, 4, 4, 64, False),
+    ("decode_gather", "bf16", 3, 1, 999, 1000, 1000, 32, 128, 100, 32, 32, 128, False),
+    ("decode_multi_query", "bf16", 2, 5, 500, 505, 512, 32, 128, 64, 16, 4, 64, False),
+    ("decode_keep_all", "bf16", 2, 1, 40, 41, 48, 32, 128, 64, 32, 32, 128, False),
+    ("decode_fp32", "fp32", 2, 2, 300, 302, 302, 4, 32, 64, 4, 4, 64, False),
+    ("integer_ties_ragged", "bf16", 1, 300, 0, 300, 300, 32, 128, 40, 8, 8, 128, True),
+    ("decode_integer_ties", "bf16", 4, 1, 2999, 3000, 3000, 32, 128, 333, 32, 32, 128, True),
+    ("long_rows_topk_lds", "bf16", 1, 9, 40000, 40009, 40009, 32, 128, 2048, 8, 8, 64, False),
+]
+
+
+def _edge_wl(e):
+    name, dt, B, T, p0, nkv, cap, HI, DI, k, H, Hkv, D, integer = e
+    return Workload(name=name, dtype=dt, batch=B, n_q=T, q_pos0=p0, n_kv=nkv, idx_heads=HI,
+                    idx_dim=DI, top_k=k, heads=H, kv_heads=Hkv, head_dim=D, seed=zlib.crc32(name.encode()) % 1000,
+                    integer_indexer=integer, qidx_std=1 / math.sqrt(DI), kidx_std=1.0,
+                    w_std=1 / math.sqrt(HI)), cap
+
+
+def _edge_inputs(wl, cap):
+    full = Workload(**{**wl.__dict__, "n_q": wl.q_pos0 + wl.n_q, "q_pos0": 0})
+    inp = make_inputs(full, "cpu", kv_capacity=cap)
+    for key in ("qidx", "w", "q"):
+        inp[key] = inp[key][:, wl.q_pos0 :].contiguous()
+    return inp
+
+
+@pytest.mark.parametrize("edge", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(edge):
+    wl, cap = _edge_wl(edge)
+    cpu = _edge_inputs(wl, cap)
+    g = _to(cpu, DEV)
+    res = _forward(g, wl, wl.top_k, wl.q_pos0, wl.n_kv, return_lse=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=wl.q_pos0, n_kv=wl.n_kv)
+    torch.cuda.synchronize()
+    assert sc.shape[-1] == dsa.lpad(wl.n_kv)
+    for b in range(wl.batch):
+        _check_sequence(wl, cpu, res, sc, b, range(wl.n_q), integer=wl.integer_indexer)
+        assert np.all(np.isneginf(to_np(sc[b])[:, wl.n_kv :]))
+
+
+@pytest.mark.parametrize("n_kv,T,top_k", [(300, 300, 37), (5000, 40, 1000), (20000, 6, 2048),
+                                          (65536, 3, 2048), (65536, 2, 65000)])
+def test_topk_kernel_on_crafted_scores(n_kv, T, top_k):
+    """The top-k op alone on float32 rows full of ties (integers in [-3, 3],
+    +-0): masks and index lists bit-exact against the oracle's selection."""
+    rng = np.random.default_rng(n_kv + T)
+    q_pos0 = n_kv - T
+    L = dsa.lpad(n_kv)
+    s = rng.integers(-3, 4, size=(1, T, L)).astype(np.float32)
+    s[rng.random(s.shape) < 0.05] = -0.0
+    s[..., :: 7] += 0.5
+    scores = torch.from_numpy(s).to(DEV)
+    mask, idx = dsa.topk_mask(scores, q_pos0=q_pos0, n_kv=n_kv, top_k=top_k)
+    torch.cuda.synchronize()
+    mask, idx = to_np(mask[0]).view(np.uint32), to_np(idx[0])
+    for i in range(T):
+        p = q_pos0 + i
+        sel = select_topk(round_scores_fp32(s[0, i]), p, top_k)
+        want = np.full(top_k, -1, dtype=np.int32)
+        want[: len(sel)] = sel
+        assert np.array_equal(idx[i], want), f"row {i}"
+        assert np.array_equal(mask[i], pack_mask(sel, n_kv)), f"row {i} mask"
+
+
+@pytest.mark.parametrize("T,q_pos0,n_kv,H,Hkv,D,dt", [(130, 20, 200, 4, 2, 128, "bf16"),
+                                                      (1, 700, 701, 8, 8, 64, "bf16"),
+                                                      (6, 300, 306, 16, 4, 128, "bf16"),
+                                                      (3, 90, 93, 4, 4, 64, "fp32")])
+def test_sparse_attention_arbitrary_masks(T, q_pos0, n_kv, H, Hkv, D, dt):
+    """The attention op alone on random masks (10% density, some empty rows,
+    bits past the query position that must be ignored)."""
+    rng = np.random.default_rng(T * 7 + n_kv)
+    gen = torch.Generator().manual_seed(T * 7 + n_kv)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    q = torch.randn(2, T, H, D, generator=gen).to(tdt)
+    k = torch.randn(2, n_kv, Hkv, D, generator=gen).to(tdt)
+    v = torch.randn(2, n_kv, Hkv, D, generator=gen).to(tdt)
+    L = dsa.lpad(n_kv)
+    bits = rng.random((2, T, L)) < 0.1
+    bits[:, :, n_kv:] = False
+    bits[0, 0] = False  # an empty row
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
+    words = (bits.reshape(2, T, L // 32, 32).astype(np.uint64) * weights).sum(-1).astype(np.uint32)
+    mask = torch.from_numpy(words.view(np.int32)).to(DEV)
+    scale = 1 / math.sqrt(D)
+    out, lse = dsa.sparse_attention(q.to(DEV), k.to(DEV), v.to(DEV), mask, q_pos0=q_pos0, n_kv=n_kv,
+                                    scale=scale, lse=True)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    from oracle import attend_selected
+    for b in range(2):
+        for i in range(T):
+            p = q_pos0 + i
+            sel = np.nonzero(bits[b, i, : p + 1])[0]
+            O, ls = attend_selected(_np64(q[b, i]), _np64(k[b]), _np64(v[b]), sel, scale)
+            assert np.abs(out[b, i] - O).max() <= OUT_TOL[dt], (b, i)
+            if sel.size == 0:
+                assert np.all(out[b, i] == 0) and np.all(np.isneginf(lse[b, i]))
+            else:
+                assert np.allclose(lse[b, i], ls, rtol=1e-4, atol=1e-3)
+
+
+def test_decode_row_equals_last_prefill_row_and_determinism():
+    wl = WORKLOADS["prefill_bf16_L4096"]
+    g = make_inputs(wl, DEV)
+    r1 = _forward(g, wl, wl.top_k, 0, wl.n_kv)
+    r2 = _forward(g, wl, wl.top_k, 0, wl.n_kv)
+    last = {k: v[:, -1:].contiguous() for k, v in g.items() if k in ("qidx", "w", "q")}
+    rd = dsa.forward(last["qidx"], last["w"], g["kidx"], last["q"], g["k"], g["v"], top_k=wl.top_k,
+                     q_pos0=wl.n_kv - 1, n_kv=wl.n_kv, scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(r1["out"], r2["out"]) and torch.equal(r1["indices"], r2["indices"])
+    assert torch.equal(rd["indices"][0, 0], r1["indices"][0, -1])
+    err = (rd["out"][0, 0].float() - r1["out"][0, -1].float()).abs().max().item()
+    assert err <= OUT_TOL["bf16"]
+
+
+def test_chunked_prefill_equals_one_shot():
+    wl = Workload(name="chunk_check", dtype="bf16", batch=1, n_q=2048, q_pos0=0, n_kv=2048, idx_heads=32,
+                  idx_dim=128, top_k=300, heads=8, kv_heads=8, head_dim=128, seed=9,
+                  qidx_std=1 / math.sqrt(128), kidx_std=1 / math.sqrt(128), w_std=1 / math.sqrt(32))
+    g = make_inputs(wl, DEV)
+    one = _forward(g, wl, wl.top_k, 0, wl.n_kv)
+    outs, idxs = [], []
+    for c in range(4):
+        sl = slice(512 * c, 512 * (c + 1))
+        r = dsa.forward(g["qidx"][:, sl], g["w"][:, sl], g["kidx"], g["q"][:, sl], g["k"], g["v"],
+                        top_k=wl.top_k, q_pos0=512 * c, n_kv=512 * (c + 1), scale=wl.scale)
+        outs.append(r["out"])
+        idxs.append(r["indices"])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(idxs, 1), one["indices"])
+    assert torch.equal(torch.cat(outs, 1), one["out"])
