@@ -1,0 +1,349 @@
+#!/usr/bin/env python3
+"""Throughput of one DSA layer (lightning indexer -> top-k mask -> sparse
+attention) on one MI355X, with the roofline fraction of its dominant kernel
+and the CPU oracle timed beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one whole layer call (dsa_forward: indexer scores, top-k bitmask
+plus index list, attention over the kept keys) over one batch of synthetic
+input that is resident in HBM before the timed region starts. The headline
+workload is single-layer prefill of one 4096-token sequence (32x128
+indexer, top_k 2048, 32x128 attention); the batched decode step (64
+sequences x 32768 cached tokens) and the chunked 65536-token prefill are
+measured in the same run and reported under "secondary". Each query is one
+token, so queries/s equals tokens/s.
+
+Per-kernel times come from HIP events recorded on the stream the kernels run
+on, around the op-level entry points (dsa_index_scores, dsa_topk_mask,
+dsa_sparse_attention), each of which launches the kernel it is named for.
+
+Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA layer queries/sec (prefill & decode) + % of MFMA / HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+HEADLINE = "prefill_bf16_L4096"
+SECONDARY = ["decode_bf16_B64_L32768", "longctx_bf16_L65536_chunk4096"]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--secondary", default=",".join(SECONDARY),
+                    help="comma-separated workloads also measured ('' for none)")
+    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="budget of the oracle timing on the host (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain device copy of 1 GiB (reference for HBM counters)")
+    ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- work accounting
+
+def causal_pairs(wl, q_pos0, n_q):
+    """sum over queries of (p + 1), the indexer's candidate pairs."""
+    p0 = q_pos0 + 1
+    return n_q * p0 + n_q * (n_q - 1) // 2
+
+
+def selected_pairs(wl, q_pos0, n_q):
+    """sum over queries of min(p + 1, top_k): the (query, kept key) pairs."""
+    tot = 0
+    k = wl.top_k
+    # rows with p + 1 <= k keep p + 1 keys, the rest keep k
+    last_small = min(q_pos0 + n_q, k) - 1  # largest p with p + 1 <= k
+    if last_small >= q_pos0:
+        n_small = last_small - q_pos0 + 1
+        tot += causal_pairs(wl, q_pos0, n_small)
+        tot += (n_q - n_small) * k
+    else:
+        tot += n_q * k
+    return tot
+
+
+def chunk_calls(wl):
+    """(q_pos0, n_q, n_kv) of each layer call of one step."""
+    if wl.chunks == 1:
+        return [(wl.q_pos0, wl.n_q, wl.n_kv)]
+    C = wl.chunk_len
+    return [(c * C, C, (c + 1) * C) for c in range(wl.chunks)]
+
+
+def op_work(wl, q_pos0, n_q, n_kv):
+    """Algorithmic work of each op for one call: the quantity its roofline
+    counts (flops for matrix-core work, bytes for bandwidth-bound work)."""
+    B, es = wl.batch, (2 if wl.dtype == "bf16" else 4)
+    HI, DI, H, Hkv, D = wl.idx_heads, wl.idx_dim, wl.heads, wl.kv_heads, wl.head_dim
+    lpad = (n_kv + 63) // 64 * 64
+    pc = B * causal_pairs(wl, q_pos0, n_q)
+    ps = B * selected_pairs(wl, q_pos0, n_q)
+    decode = n_q <= 8
+    peak_mfma = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_MFMA_TFLOPS
+    res = {}
+    # indexer: 2*HI*DI flops per causal pair; decode reads each cached index key once
+    idx_bytes = B * n_kv * DI * es + B * n_q * (HI * DI * es + HI * 4) + B * n_q * lpad * 4
+    if decode:
+        res["index_scores"] = dict(bound="hbm", work=idx_bytes, unit="GB/s", peak=PEAK_HBM_GBS)
+    else:
+        res["index_scores"] = dict(bound="mfma", work=2.0 * HI * DI * pc, unit="TFLOP/s", peak=peak_mfma)
+    # top-k: reads every candidate score once, writes the mask and the index list
+    topk_bytes = 4 * pc + B * n_q * (lpad // 8) + B * n_q * wl.top_k * 4
+    res["topk_mask"] = dict(bound="hbm", work=topk_bytes, unit="GB/s", peak=PEAK_HBM_GBS)
+    # attention: 4*H*D flops per selected pair; decode gathers the kept K/V rows
+    if decode:
+        attn_bytes = ps * 2 * Hkv * D * es + 2 * B * n_q * H * D * es + B * n_q * (lpad // 8)
+        res["sparse_attention"] = dict(bound="hbm", work=attn_bytes, unit="GB/s", peak=PEAK_HBM_GBS)
+    else:
+        res["sparse_attention"] = dict(bound="mfma", work=4.0 * H * D * ps, unit="TFLOP/s", peak=peak_mfma)
+    return res, pc, ps
+
+
+# ----------------------------------------------------------------------------- GPU timing
+
+def run_gpu(wl, steps, warmup, torch, dsa, make_inputs):
+    dev = torch.device("cuda:0")
+    log(f"[bench] {wl.name}: drawing inputs on the GPU")
+    g = make_inputs(wl, dev)
+    torch.cuda.synchronize()
+    calls = chunk_calls(wl)
+    B, H, D = wl.batch, wl.heads, wl.head_dim
+    out = torch.empty_like(g["q"])
+    idx = torch.empty((B, wl.n_q, wl.top_k), dtype=torch.int32, device=dev)
+    # one workspace sized for the largest call
+    big = calls[-1]
+    dims = dsa.make_dims(batch=B, n_q=big[1], q_pos0=big[0], n_kv=big[2], kv_capacity=g["k"].shape[1],
+                         idx_heads=wl.idx_heads, idx_dim=wl.idx_dim, top_k=wl.top_k, heads=H,
+                         kv_heads=wl.kv_heads, head_dim=D, scale=wl.scale,
+                         dtype=dsa.DSA_BF16 if wl.dtype == "bf16" else dsa.DSA_FP32)
+    ws_bytes = max(dsa.workspace_size(dims, dsa.DSA_OP_FORWARD),
+                   dsa.workspace_size(dims, dsa.DSA_OP_SPARSE_ATTENTION), 256)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+
+    def views(q0, nq):
+        sl = slice(q0 - wl.q_pos0, q0 - wl.q_pos0 + nq)
+        return (g["qidx"][:, sl], g["w"][:, sl], g["q"][:, sl], out[:, sl], idx[:, sl])
+
+    call_views = [views(q0, nq) for (q0, nq, _) in calls]
+
+    def step():
+        for (q0, nq, nkv), (qi, wi, qq, oo, ii) in zip(calls, call_views):
+            dsa.forward(qi, wi, g["kidx"], qq, g["k"], g["v"], top_k=wl.top_k, q_pos0=q0, n_kv=nkv,
+                        scale=wl.scale, workspace=ws, out=oo, indices=ii)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / steps
+
+    # Per-op times: the same calls through the op-level entry points, HIP
+    # events on the stream they are launched on.
+    stream = torch.cuda.current_stream(dev)
+    Lmax = (big[2] + 63) // 64 * 64
+    scores = torch.empty((B, big[1], Lmax), dtype=torch.float32, device=dev)
+    mask = torch.empty((B, big[1], Lmax // 32), dtype=torch.int32, device=dev)
+    op_ms = {"index_scores": 0.0, "topk_mask": 0.0, "sparse_attention": 0.0}
+    op_work_tot = {}
+    n_rep = max(1, min(steps, 10))
+    for rep in range(n_rep + 1):  # rep 0 warms up
+        for (q0, nq, nkv), (qi, wi, qq, oo, ii) in zip(calls, call_views):
+            lp = (nkv + 63) // 64 * 64
+            sc = scores[:, :nq, :lp] if (nq, lp) != (big[1], Lmax) else scores
+            mk = mask[:, :nq, : lp // 32] if (nq, lp) != (big[1], Lmax) else mask
+            if not sc.is_contiguous():
+                sc = torch.empty((B, nq, lp), dtype=torch.float32, device=dev)
+                mk = torch.empty((B, nq, lp // 32), dtype=torch.int32, device=dev)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record(stream)
+            dsa.index_scores(qi, wi, g["kidx"], q_pos0=q0, n_kv=nkv, out=sc)
+            ev[1].record(stream)
+            mk2, _ = dsa.topk_mask(sc, q_pos0=q0, n_kv=nkv, top_k=wl.top_k, indices=True,
+                                   mask_out=mk, indices_out=ii)
+            ev[2].record(stream)
+            dsa.sparse_attention(qq, g["k"], g["v"], mk2, q_pos0=q0, n_kv=nkv, scale=wl.scale,
+                                 workspace=ws, out=oo)
+            ev[3].record(stream)
+            ev[3].synchronize()
+            if rep > 0:
+                for j, name in enumerate(("index_scores", "topk_mask", "sparse_attention")):
+                    op_ms[name] += ev[j].elapsed_time(ev[j + 1]) / n_rep
+                w_, _, _ = op_work(wl, q0, nq, nkv)
+                for name, info in w_.items():
+                    op_work_tot.setdefault(name, dict(info, work=0.0))
+                    op_work_tot[name]["work"] += info["work"] / n_rep
+    kernels = []
+    for name, ms in op_ms.items():
+        info = op_work_tot[name]
+        scale = 1e-9 if info["unit"] == "GB/s" else 1e-12
+        achieved = info["work"] * scale / (ms * 1e-3)
+        kernels.append({"op": name, "ms_per_step": round(ms, 4), "bound": info["bound"],
+                        "achieved": round(achieved, 2), "peak": info["peak"], "unit": info["unit"],
+                        "frac": round(achieved / info["peak"], 4),
+                        "work_per_step": info["work"],
+                        "work_unit": "bytes" if info["unit"] == "GB/s" else "flop"})
+    dominant = max(kernels, key=lambda k: k["ms_per_step"])
+    queries = wl.batch * wl.n_q
+    del g, out, idx, ws, scores, mask
+    torch.cuda.empty_cache()
+    return {
+        "workload": wl.name,
+        "queries_per_step": queries,
+        "ms_per_step": ms_per_step,
+        "value": queries / (ms_per_step * 1e-3),
+        "kernels": kernels,
+        "dominant": dominant,
+        "calls_per_step": len(calls),
+    }
+
+
+# ----------------------------------------------------------------------------- CPU oracle timing
+
+def cpu_baseline(wl, budget_s, torch, make_inputs):
+    """The oracle as it stands, on seeded rows of the same workload, until the
+    time budget is spent. Inputs are drawn on the host with the same recipe."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from dsa_workloads import sample_rows
+    from oracle import dsa_rows
+
+    log(f"[bench] oracle on the host: {wl.name}, ~{budget_s:.0f} s")
+    cpu = make_inputs(wl, "cpu")
+    f64 = lambda t: t[0].float().numpy().astype(np.float64)
+    qidx, w, kidx, q, k, v = (f64(cpu[n]) for n in ("qidx", "w", "kidx", "q", "k", "v"))
+    rows = sample_rows(wl, wl.n_q, seed=4321)
+    rng = np.random.default_rng(4321)
+    rows = list(rng.permutation(np.asarray(rows)))
+    done = 0
+    t0 = time.perf_counter()
+    for i in rows:
+        dsa_rows(qidx, w, kidx, q, k, v, wl.q_pos0, wl.top_k, wl.scale, rows=[int(i)])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s and done >= 8:
+            break
+    dt = time.perf_counter() - t0
+    threads = 1
+    for pool in threadpool_info():
+        if pool.get("user_api") == "blas":
+            threads = max(threads, int(pool.get("num_threads", 1)))
+    return {
+        "value": done / dt,
+        "unit": "queries/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} seeded random query rows of {wl.name} (whole layer per row: float64 "
+                  f"scores, float32-rounded top-k selection, attention over the kept keys), "
+                  f"{dt:.1f} s wall",
+    }
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(this DSA layer build runs on a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dsa_lightning_indexer_03_amd as dsa
+    from dsa_workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dsa.lib()  # fails loudly if libdsa.so is missing
+
+    wl = WORKLOADS[args.workload]
+    head = run_gpu(wl, args.steps, args.warmup, torch, dsa, make_inputs)
+    log(f"[bench] {wl.name}: {head['ms_per_step']:.3f} ms/step, {head['value']:.4g} queries/s")
+    secondary = []
+    for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
+        r = run_gpu(WORKLOADS[name], args.secondary_steps, min(args.warmup, 2), torch, dsa, make_inputs)
+        log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step, {r['value']:.4g} queries/s")
+        secondary.append({
+            "workload": name, "value": r["value"], "unit": "queries/s",
+            "ms_per_step": round(r["ms_per_step"], 4), "steps": args.secondary_steps,
+            "roofline": _roofline(r["dominant"]), "kernels": r["kernels"],
+        })
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB written by one device copy")
+        del src, dst
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(wl, args.cpu_seconds, torch, make_inputs)
+    line = {
+        "metric": METRIC,
+        "value": head["value"],
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "n_q": wl.n_q, "q_pos0": wl.q_pos0,
+            "n_kv": wl.n_kv, "chunks": wl.chunks, "indexer": f"{wl.idx_heads}x{wl.idx_dim}",
+            "top_k": wl.top_k, "attention": f"{wl.heads}x{wl.head_dim}", "kv_heads": wl.kv_heads,
+            "tokens_per_s": head["value"],
+        },
+        "roofline": _roofline(head["dominant"]),
+        "cpu_baseline": cpu,
+        "kernels": head["kernels"],
+        "secondary": secondary,
+        "device": torch.cuda.get_device_name(0),
+    }
+    text = json.dumps(line)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(text + "\n")
+    print(text, flush=True)
+
+
+def _roofline(k):
+    return {"bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"], "unit": k["unit"],
+            "frac": k["frac"], "traffic": None, "kernel": k["op"]}
+
+
+if __name__ == "__main__":
+    main()

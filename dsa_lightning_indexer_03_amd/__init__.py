@@ -111,6 +111,18 @@ def _need_gpu(*ts):
             raise ValueError("DSA tensors must be contiguous")
 
 
+def _expect(name, t, shape, dtype=None):
+    """Shape (and dtype) check before any pointer reaches the library: the C
+    ABI sees raw pointers only, so a wrong extent here would become an
+    out-of-bounds access on the device."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -144,6 +156,9 @@ def index_scores(qidx, w, kidx, *, q_pos0=0, n_kv=None, out=None):
     B, T, HI, DI = qidx.shape
     cap = kidx.shape[1]
     n_kv = cap if n_kv is None else n_kv
+    _expect("w", w, (B, T, HI), torch.float32)
+    _expect("kidx", kidx, (B, cap, DI), qidx.dtype)
+    _expect("out", out, (B, T, lpad(n_kv)), torch.float32)
     d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, idx_heads=HI,
                   idx_dim=DI, dtype=_dtype_code(qidx))
     if out is None:
@@ -153,29 +168,41 @@ def index_scores(qidx, w, kidx, *, q_pos0=0, n_kv=None, out=None):
     return out
 
 
-def topk_mask(scores, *, q_pos0=0, n_kv, top_k, indices=True):
-    """(mask [B, T, Lpad/32] int32 bit patterns, indices [B, T, top_k] int32 or None)."""
-    _need_gpu(scores)
+def topk_mask(scores, *, q_pos0=0, n_kv, top_k, indices=True, mask_out=None, indices_out=None):
+    """(mask [B, T, Lpad/32] int32 bit patterns, indices [B, T, top_k] int32 or None).
+    `mask_out` / `indices_out` are written instead of allocating when given."""
+    _need_gpu(scores, mask_out, indices_out)
     B, T, L = scores.shape
     d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=n_kv, top_k=top_k)
     if L != lpad(n_kv):
         raise ValueError(f"scores rows must have {lpad(n_kv)} entries")
-    mask = torch.empty((B, T, L // 32), dtype=torch.int32, device=scores.device)
-    idx = torch.empty((B, T, top_k), dtype=torch.int32, device=scores.device) if indices else None
+    _expect("mask_out", mask_out, (B, T, L // 32), torch.int32)
+    _expect("indices_out", indices_out, (B, T, top_k), torch.int32)
+    mask = mask_out if mask_out is not None else torch.empty((B, T, L // 32), dtype=torch.int32,
+                                                              device=scores.device)
+    idx = indices_out
+    if idx is None and indices:
+        idx = torch.empty((B, T, top_k), dtype=torch.int32, device=scores.device)
     _check(lib().dsa_topk_mask(ctypes.byref(d), _ptr(scores), _ptr(mask), _ptr(idx), None, 0,
                                _stream(scores)))
     return mask, idx
 
 
-def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=False, workspace=None):
-    """out [B, T, H, D] (and lse [B, T, H] float32) over the masked-in keys."""
-    _need_gpu(q, k, v, mask, workspace)
+def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=False, workspace=None,
+                     out=None):
+    """out [B, T, H, D] (and lse [B, T, H] float32) over the masked-in keys.
+    `out` is written instead of allocating when given."""
+    _need_gpu(q, k, v, mask, workspace, out)
     B, T, H, D = q.shape
     cap, Hkv = k.shape[1], k.shape[2]
     n_kv = cap if n_kv is None else n_kv
+    _expect("k", k, (B, cap, Hkv, D), q.dtype)
+    _expect("v", v, (B, cap, Hkv, D), q.dtype)
+    _expect("mask", mask, (B, T, lpad(n_kv) // 32), torch.int32)
     d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, heads=H,
                   kv_heads=Hkv, head_dim=D, scale=scale, dtype=_dtype_code(q))
-    out = torch.empty_like(q)
+    _expect("out", out, (B, T, H, D), q.dtype)
+    out = torch.empty_like(q) if out is None else out
     lse_t = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if lse else None
     ws, nbytes = _workspace(d, DSA_OP_SPARSE_ATTENTION, q.device, workspace)
     _check(lib().dsa_sparse_attention(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(mask),
@@ -184,25 +211,39 @@ def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=Fals
 
 
 def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
-            return_indices=True, return_mask=False, return_lse=False, workspace=None, out=None):
+            return_indices=True, return_mask=False, return_lse=False, workspace=None, out=None,
+            indices=None, mask=None, lse=None):
     """The whole DSA layer. Returns a dict with 'out' and the requested extras
-    ('indices' [B, T, top_k] int32, 'mask' [B, T, Lpad/32] int32, 'lse')."""
-    _need_gpu(qidx, w, kidx, q, k, v, workspace, out)
+    ('indices' [B, T, top_k] int32, 'mask' [B, T, Lpad/32] int32, 'lse').
+    Passing `out`, `indices`, `mask`, `lse` or `workspace` tensors makes the
+    call write into them instead of allocating (each passed extra is also
+    returned)."""
+    _need_gpu(qidx, w, kidx, q, k, v, workspace, out, indices, mask, lse)
     B, T, HI, DI = qidx.shape
     H, D = q.shape[2], q.shape[3]
     cap, Hkv = k.shape[1], k.shape[2]
     n_kv = cap if n_kv is None else n_kv
+    _expect("w", w, (B, T, HI), torch.float32)
+    _expect("kidx", kidx, (B, cap, DI), qidx.dtype)
+    _expect("q", q, (B, T, H, D), qidx.dtype)
+    _expect("k", k, (B, cap, Hkv, D), q.dtype)
+    _expect("v", v, (B, cap, Hkv, D), q.dtype)
+    _expect("out", out, (B, T, H, D), q.dtype)
     d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, idx_heads=HI,
                   idx_dim=DI, top_k=top_k, heads=H, kv_heads=Hkv, head_dim=D, scale=scale,
                   dtype=_dtype_code(q))
     dev = q.device
     res = {"out": torch.empty_like(q) if out is None else out}
-    if return_indices:
-        res["indices"] = torch.empty((B, T, top_k), dtype=torch.int32, device=dev)
-    if return_mask:
-        res["mask"] = torch.empty((B, T, lpad(n_kv) // 32), dtype=torch.int32, device=dev)
-    if return_lse:
-        res["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=dev)
+    extras = (("indices", indices, return_indices, (B, T, top_k), torch.int32),
+              ("mask", mask, return_mask, (B, T, lpad(n_kv) // 32), torch.int32),
+              ("lse", lse, return_lse, (B, T, H), torch.float32))
+    for name, given, wanted, shape, dt in extras:
+        if given is not None:
+            if tuple(given.shape) != shape or given.dtype != dt:
+                raise ValueError(f"{name} must be {dt} of shape {shape}")
+            res[name] = given
+        elif wanted:
+            res[name] = torch.empty(shape, dtype=dt, device=dev)
     ws, nbytes = _workspace(d, DSA_OP_FORWARD, dev, workspace)
     _check(lib().dsa_forward(ctypes.byref(d), _ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k),
                              _ptr(v), _ptr(res["out"]), _ptr(res.get("lse")),
