@@ -553,6 +553,7 @@ bool gather_supported(int H, int D) {
 
 hipError_t launch_attn_prefill(const AttnParams& p, int dtype, int D, hipStream_t st) {
   if (dtype == 1) {
+    if (attn_prefill_bf16_supported(D)) return launch_attn_prefill_bf16(p, st);
     if (D == 128) return launch_prefill_t<bf16, 128>(p, st);
     if (D == 64) return launch_prefill_t<bf16, 64>(p, st);
   } else {
