@@ -6,16 +6,20 @@
 // attention is the masked flash-attention path it feeds [aiaulis paras 2 and
 // 4; devotd section 2].
 //
-// Work split. A workgroup is 4 waves x 64 queries of one (sequence, head);
-// 64-key tiles of K and V stream through LDS, double-buffered. Each wave
-// keeps its 64 query rows in registers (4 blocks of 16) and reads every K and
-// V fragment from LDS once per tile, using it for all four query blocks, so
-// LDS traffic is 512 B per key per wave against 64 * 512 flops of matrix
-// work per key: half of what 32-query waves need.
+// Work split. A workgroup is 4 waves of one (sequence, head); each wave owns
+// 32 query rows (two blocks of 16, Q^T fragments in registers) and 64-key
+// tiles of K and V stream through LDS, double-buffered. Every K and V
+// fragment a wave reads from LDS is used for both of its query blocks (512 B
+// of LDS reads per key per wave against 32 * 512 flops of matrix work). At
+// at most 256 registers per lane two workgroups share a CU, two waves per
+// SIMD, so one wave's softmax overlaps the other's matrix work. (Waves of 64
+// queries halve the LDS traffic but need more than 256 registers: their
+// accumulators then live in AGPRs, which the compiler copies around every
+// tile, and they measured slower.)
 //
 // Matrix layout (v_mfma_f32_16x16x32_bf16, see dsa_device.hpp):
-//   S^T = K Q^T   A = K rows from LDS, B = Q^T from registers; lane (c, g)
-//                 ends up holding keys 16*kb + 4*g + r (r = 0..3) of query c.
+//   S^T = K Q^T   A = K rows from LDS, B = Q^T; lane (c, g) ends up holding
+//                 keys 16*kb + 4*g + r (r = 0..3) of query c.
 //   O^T += V^T P^T  the S^T accumulators, exponentiated and rounded to bf16,
 //                 are used in place as the B operand; V^T is stored in LDS so
 //                 that the 8 keys a lane feeds per k-step are contiguous.
@@ -27,8 +31,9 @@
 // bitfield insert per element, exponentiated with exp2 against a running
 // maximum that is only raised (and O rescaled) when a tile's maximum exceeds
 // it by more than 2^8; until then probabilities stay <= 256, which float32
-// sums and bf16 P carry without loss. The final normalisation divides by the
-// sum taken against the same maximum, so the result is exact softmax.
+// sums and bf16 P carry without loss. The row sum is taken over the bf16
+// probabilities that enter P V (two per dot2 instruction), and the final
+// normalisation divides by it, so the result is softmax over the kept keys.
 //
 // Scheduling. Workgroup ids are mapped so that all query tiles of one
 // (sequence, head) pair land on the same XCD (id mod 8), sharing its L2 for
@@ -40,9 +45,6 @@ namespace dsa {
 namespace {
 
 constexpr int kD = 128;             // head dim
-constexpr int kQB = 4;              // 16-query blocks per wave
-constexpr int kQW = 16 * kQB;       // queries per wave
-constexpr int kQT = 4 * kQW;        // queries per workgroup
 constexpr int kKT = 64;             // keys per tile
 constexpr int kKS = kD / 32;        // k-steps of S^T (head dim / 32)
 constexpr int kDB = kD / 16;        // 16-dim blocks of O^T
@@ -50,10 +52,12 @@ constexpr int kKPitch = kD * 2 + 16;         // bytes per K row in LDS (padded)
 constexpr int kKBytes = kKT * kKPitch;
 constexpr int kVBytes = kD * kKT * 2;        // V^T: kD rows of 64 keys, 128 B each
 constexpr int kStage = kKBytes + kVBytes;
-constexpr int kQPitch = kD * 2 + 16;         // bytes per Q row in LDS (padded)
-constexpr int kQBytes = kQT * kQPitch;
 constexpr float kLazyMax = 8.0f;             // log2 units
 constexpr float kLn2f = 0.69314718055994530942f;
+
+constexpr int kQB = 2;               // 16-query blocks per wave
+constexpr int kQW = 16 * kQB;        // queries per wave
+constexpr int kQT = 4 * kQW;        // queries per workgroup
 
 // 16-byte column of V^T row d that holds logical column `chunk` (0..7).
 __device__ __forceinline__ int vt_chunk(int d, int chunk) { return chunk ^ ((d ^ (d >> 3)) & 7); }
@@ -70,9 +74,18 @@ __device__ __forceinline__ float mask_elem(float s, uint32_t word, int bit) {
   return __int_as_float((m & __float_as_int(s)) | (~m & (int)0xff800000u));
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float sum8_bf16(const bf16x8& p, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, acc, false);
+  return acc;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStage + kQBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStage];
 
   const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
   const int qi = slot / pairs_per_xcd, pair = (slot % pairs_per_xcd) * 8 + xcd;
@@ -84,7 +97,7 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   const int t_end = min(t0 + kQT, a.T);
   const int n_tiles = (a.q_pos0 + t_end - 1) / kKT + 1;
   const int nwords = a.Lpad / 32;
-  const int tw = t0 + wave * kQW;                  // first query of this wave
+  const int tw = t0 + wave * kQW;                // first query of this wave
   const bool wave_live = tw < a.T;
   const int pw_first = a.q_pos0 + tw;
   const int pw_last = a.q_pos0 + min(tw + kQW, a.T) - 1;
@@ -92,27 +105,23 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   const size_t kv_tok = (size_t)a.Hkv * kD;        // elements per cached token
   const bf16* kbase = static_cast<const bf16*>(a.k) + (size_t)b * a.kv_cap * kv_tok + (size_t)hk * kD;
   const bf16* vbase = static_cast<const bf16*>(a.v) + (size_t)b * a.kv_cap * kv_tok + (size_t)hk * kD;
+  // Query rows past the end read the last row (finite data, never stored).
+  const bf16* qsrc = static_cast<const bf16*>(a.q) + ((size_t)b * a.T * a.H + h) * kD;
 
-  // The wave's 64 query rows go to its own slice of LDS (rows past the end
-  // copy the last row: finite data, never stored); Q^T fragments (query
-  // 16*qb + c, dims 32*kk + 8*g + e) are read from there for every tile.
-  unsigned char* qlds = lds + 2 * kStage + wave * kQW * kQPitch;
-  {
-    const bf16* qsrc = static_cast<const bf16*>(a.q) + ((size_t)b * a.T * a.H + h) * kD;
+  // Q^T operands: query 16*qb + c of the wave, dims 32*kk + 8*g + e.
+  bf16x8 qreg[kQB][kKS];
 #pragma unroll
-    for (int n = 0; n < kQW * 16 / 64; ++n) {
-      const int i = lane + 64 * n, row = i >> 4, ch = i & 15;
-      const int t = min(tw + row, a.T - 1);
-      *reinterpret_cast<u32x4*>(qlds + row * kQPitch + ch * 16) =
-          *reinterpret_cast<const u32x4*>(qsrc + (size_t)t * a.H * kD + ch * 8);
-    }
+  for (int qb = 0; qb < kQB; ++qb) {
+    const bf16* qp = qsrc + (size_t)min(tw + 16 * qb + c, a.T - 1) * a.H * kD;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) qreg[qb][kk] = load_frag<bf16>(qp + 32 * kk + 8 * g);
   }
   int tq[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) tq[qb] = tw + 16 * qb + c;
   // Mask row of query block 0; block qb is 16 * qb rows further.
   const uint32_t* mrow0 = a.mask + ((size_t)b * a.T + min(tw + c, a.T - 1)) * nwords;
-  const int last_row_off = (a.T - 1 - min(tw + c, a.T - 1));  // rows to the last valid one
+  const int last_row_off = a.T - 1 - min(tw + c, a.T - 1);  // rows to the last valid one
 
   f32x4 o[kDB][kQB];
 #pragma unroll
@@ -128,22 +137,34 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
 
   // Tile loaders. K: 1024 16-B chunks, 4 per thread (chunk i = tid + 256 n:
   // key i / 16, column i % 16). V: thread (kq = tid / 16, dc = tid % 16)
-  // loads dims 8*dc..8*dc+7 of keys 4*kq..4*kq+3.
+  // loads dims 8*dc..8*dc+7 of keys 4*kq..4*kq+3. Keys past n_kv (last tile
+  // only) read the last cached row instead: finite data the mask gives zero
+  // weight.
   const int v_kq = tid >> 4, v_dc = tid & 15;
+  const size_t tile_stride = (size_t)kKT * kv_tok;
+  const bf16* kp = kbase + (size_t)(tid >> 4) * kv_tok + (tid & 15) * 8;  // + 16 keys per n
+  const bf16* vp = vbase + (size_t)(4 * v_kq) * kv_tok + v_dc * 8;         // + 1 key per j
   u32x4 kst[4], vst[4];
   auto gload = [&](int tile) {
     const int s0 = tile * kKT;
-    // Keys past n_kv read the last cached row: finite data that the mask
-    // (bits only for s <= p < n_kv) gives zero weight.
+    if (s0 + kKT <= a.n_kv) {
+      const bf16* kt = kp + tile * tile_stride;
+      const bf16* vt = vp + tile * tile_stride;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int i = tid + n * 256, key = i >> 4, ch = i & 15, s = min(s0 + key, a.n_kv - 1);
-      kst[n] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s * kv_tok + ch * 8);
-    }
+      for (int n = 0; n < 4; ++n) kst[n] = *reinterpret_cast<const u32x4*>(kt + (size_t)(16 * n) * kv_tok);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = min(s0 + 4 * v_kq + j, a.n_kv - 1);
-      vst[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)s * kv_tok + v_dc * 8);
+      for (int j = 0; j < 4; ++j) vst[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)j * kv_tok);
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int s = min(s0 + (tid >> 4) + 16 * n, a.n_kv - 1);
+        kst[n] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s * kv_tok + (tid & 15) * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = min(s0 + 4 * v_kq + j, a.n_kv - 1);
+        vst[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)s * kv_tok + v_dc * 8);
+      }
     }
   };
   auto lstore = [&](int buf) {
@@ -221,19 +242,14 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
           for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < kKS; ++kk) {
-          bf16x8 qf[kQB];
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb)
-            qf[qb] = *reinterpret_cast<const bf16x8*>(qlds + (16 * qb + c) * kQPitch + (4 * kk + g) * 16);
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + (16 * kb + c) * kKPitch + (4 * kk + g) * 16);
 #pragma unroll
-            for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = mma_kstep(kf, qf[qb], sacc[kb][qb]);
+            for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = mma_kstep(kf, qreg[qb][kk], sacc[kb][qb]);
           }
         }
-        // Softmax of each query block; P^T in bf16, in the accumulator layout.
-        bf16x8 pf[kQB][2];
+        // Masked maxima; the running maximum is raised lazily.
         bool need_any = false;
         float mx_all[kQB];
 #pragma unroll
@@ -244,8 +260,7 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
           for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              float v = sacc[kb][qb][r];
-              v = mask_elem(v, kb < 2 ? wlo : whi, 16 * (kb & 1) + r);
+              const float v = mask_elem(sacc[kb][qb][r], kb < 2 ? wlo : whi, 16 * (kb & 1) + r);
               sacc[kb][qb][r] = v;
               mx = fmaxf(mx, v);
             }
@@ -264,24 +279,22 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
             for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
           }
         }
+        // P^T in bf16, in the accumulator layout; row sums over the bf16 values.
+        bf16x8 pf[kQB][2];
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
           const float m_use = m_run[qb] == fneg_inf() ? 0.f : m_run[qb];
-          float ps = 0.f;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             bf16x8 pv;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], sl2, -m_use));
-                ps += e;
-                pv[4 * hf + r] = (bf16)e;
-              }
+              for (int r = 0; r < 4; ++r)
+                pv[4 * hf + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], sl2, -m_use));
             pf[qb][ks] = pv;
+            l_run[qb] = sum8_bf16(pv, l_run[qb]);
           }
-          l_run[qb] += ps;
         }
         // O^T += V^T P^T
 #pragma unroll
@@ -336,7 +349,8 @@ hipError_t launch_attn_prefill_bf16(const AttnParams& p, hipStream_t st) {
   const int pairs_per_xcd = (pairs + 7) / 8;
   const long long nblocks = 8ll * n_qtiles * pairs_per_xcd;
   if (nblocks > 0x7fffffffll) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_prefill_bf16_kernel, dim3((unsigned)nblocks), dim3(256), 0, st, p, n_qtiles, pairs_per_xcd);
+  hipLaunchKernelGGL(attn_prefill_bf16_kernel, dim3((unsigned)nblocks), dim3(256), 0, st, p, n_qtiles,
+                     pairs_per_xcd);
   return hipGetLastError();
 }
 

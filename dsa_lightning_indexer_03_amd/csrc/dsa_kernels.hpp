@@ -39,7 +39,7 @@ struct AttnParams {
   float scale_log2;      // softmax scale * log2(e)
 };
 hipError_t launch_attn_prefill(const AttnParams& p, int dtype, int D, hipStream_t st);
-// bf16, head dim 128: 64 queries per wave, register-transposed V (attn_prefill_bf16.hip).
+// bf16, head dim 128: 32 queries per wave, register-transposed V (attn_prefill_bf16.hip).
 bool attn_prefill_bf16_supported(int D);
 hipError_t launch_attn_prefill_bf16(const AttnParams& p, hipStream_t st);
 

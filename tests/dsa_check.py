@@ -14,6 +14,11 @@ Tolerances:
   * Attention output: max abs error 2e-2 for bf16 I/O, 1e-4 for fp32 I/O,
     against the oracle's attention over the GPU's own kept set (equal to the
     oracle's set wherever the sets agree).
+  * Log-sum-exp: with bf16 I/O the kernels sum the probabilities as they
+    enter P V, rounded to bf16 (relative error <= 2^-9 each), so the sum is
+    within a factor (1 +- 2^-9) of the exact one and |lse error| <=
+    -log(1 - 2^-9) < 1.96e-3; the tolerance is 2.5e-3 absolute. fp32 I/O
+    keeps float32 probabilities: 1e-3.
 """
 from __future__ import annotations
 
@@ -24,6 +29,7 @@ from oracle import attend_selected, index_scores, round_scores_fp32, select_topk
 
 U32 = 2.0 ** -24
 OUT_TOL = {"bf16": 2e-2, "fp32": 1e-4}
+LSE_ATOL = {"bf16": 2.5e-3, "fp32": 1e-3}
 
 
 def to_np(t: torch.Tensor) -> np.ndarray:
@@ -117,6 +123,6 @@ class RowChecker:
             self.stats["max_out_err"] = max(self.stats["max_out_err"], err)
             assert err <= OUT_TOL[self.dtype], f"row {i}: output error {err}"
             if gpu_lse is not None:
-                assert np.allclose(gpu_lse, lse, rtol=1e-4, atol=1e-3), f"row {i}: lse mismatch"
+                assert np.allclose(gpu_lse, lse, rtol=1e-4, atol=LSE_ATOL[self.dtype]), f"row {i}: lse mismatch"
         self.stats["rows"] += 1
         return ora_sel
