@@ -454,29 +454,26 @@ __global__ __launch_bounds__(256) void attn_gather_partial_kernel(GatherParams a
   }
 }
 
+// One workgroup per (head, query row), one thread per output dim: the split
+// partials of that head are merged by their log-sum-exp.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_gather_combine_kernel(GatherParams a) {
-  const int row = blockIdx.x;
+__global__ __launch_bounds__(D) void attn_gather_combine_kernel(GatherParams a) {
+  const int h = blockIdx.x, row = blockIdx.y, d = threadIdx.x;
   const int b = row / a.T, t = row % a.T, p = a.q_pos0 + t;
   const int count = a.counts ? a.counts[row] : min(a.top_k, p + 1);
   const int ns = (count + kGatherSplit - 1) / kGatherSplit;
-  const float* ml = a.part_ml + (size_t)row * a.n_splits * a.H * 2;
-  const float* po = a.part_o + (size_t)row * a.n_splits * a.H * D;
-  T* orow = static_cast<T*>(a.out) + ((size_t)b * a.T + t) * a.H * D;
-  for (int i = threadIdx.x; i < a.H * D; i += 256) {
-    const int h = i / D;
-    float M = fneg_inf();
-    for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[((size_t)j * a.H + h) * 2]);
-    float L = 0.f, O = 0.f;
-    for (int j = 0; j < ns; ++j) {
-      const float f = __builtin_amdgcn_exp2f(ml[((size_t)j * a.H + h) * 2] - M);
-      L += f * ml[((size_t)j * a.H + h) * 2 + 1];
-      O += f * po[((size_t)j * a.H + h) * D + (i % D)];
-    }
-    orow[i] = from_float<T>(L > 0.f ? O / L : 0.f);
-    if (a.lse && (i % D) == 0)
-      a.lse[((size_t)b * a.T + t) * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : fneg_inf();
+  const float* ml = a.part_ml + (size_t)row * a.n_splits * a.H * 2 + 2 * h;
+  const float* po = a.part_o + (size_t)row * a.n_splits * a.H * D + (size_t)h * D + d;
+  float M = fneg_inf();
+  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[(size_t)j * a.H * 2]);
+  float L = 0.f, O = 0.f;
+  for (int j = 0; j < ns; ++j) {
+    const float f = __builtin_amdgcn_exp2f(ml[(size_t)j * a.H * 2] - M);
+    L += f * ml[(size_t)j * a.H * 2 + 1];
+    O += f * po[(size_t)j * a.H * D];
   }
+  static_cast<T*>(a.out)[(((size_t)b * a.T + t) * a.H + h) * D + d] = from_float<T>(L > 0.f ? O / L : 0.f);
+  if (a.lse && d == 0) a.lse[((size_t)b * a.T + t) * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : fneg_inf();
 }
 
 // One workgroup per row: tokens s <= p (and < n_kv) whose mask bit is set,
@@ -529,7 +526,7 @@ hipError_t launch_gather_hw(const GatherParams& p, hipStream_t st) {
   hipLaunchKernelGGL((attn_gather_partial_kernel<T, D, HW>), dim3(p.n_splits, p.B * p.T), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_gather_combine_kernel<T, D>), dim3(p.B * p.T), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((attn_gather_combine_kernel<T, D>), dim3(p.H, p.B * p.T), dim3(D), 0, st, p);
   return hipGetLastError();
 }
 

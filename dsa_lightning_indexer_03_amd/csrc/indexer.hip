@@ -29,6 +29,11 @@ namespace {
 
 constexpr int QPW = 4;  // queries per wave (the swap-based head sum packs up to four)
 
+// max(x, 0) as one integer max on the bit pattern: negative floats (and -0)
+// are negative as int32, so they become +0; non-negative floats pass
+// unchanged. One instruction, where fmaxf also quiets NaNs first.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <typename T, int DI, int NQ>
 struct QueryFrags {
   static constexpr int KSTEPS = DI / 32;
@@ -66,24 +71,36 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
 // Scores of the wave's (up to 4) queries against one 16-key subtile whose B
 // operands (keys (l%16), dims 32*kk + 8*(l/16) + e) are in bf. Returns the
 // score of query j(lane) = 2*(g&1) + (g>>1) and key (l%16).
+// Queries past the end and heads past H_I have zero operands and zero
+// weights, so they add exact zeros; every query and both head blocks are
+// computed unconditionally, the 2*NQ accumulator chains interleaved per k-step.
 template <typename T, int DI, int NQ>
 __device__ __forceinline__ float score_subtile(const QueryFrags<T, DI, NQ>& f,
-                                               const frag_t<T> (&bf)[DI / 32], int nq,
-                                               bool two_row_blocks) {
+                                               const frag_t<T> (&bf)[DI / 32]) {
+  f32x4 acc[NQ][2];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[j][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < DI / 32; ++kk) {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) acc[j][rb] = mma_kstep(f.a[j][rb][kk], bf[kk], acc[j][rb]);
+    // keep the 2*NQ independent chains interleaved (the scheduler would
+    // otherwise run them one after another, exposing the MFMA latency)
+    __builtin_amdgcn_sched_barrier(0);
+  }
   float part[QPW];
 #pragma unroll
   for (int j = 0; j < QPW; ++j) {
     part[j] = 0.f;
-    if (j < NQ && j < nq) {
+    if (j < NQ) {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        if (rb == 1 && !two_row_blocks) break;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int kk = 0; kk < DI / 32; ++kk) acc = mma_kstep(f.a[j][rb][kk], bf[kk], acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[j] = fmaf(f.w[j][rb][r], fmaxf(acc[r], 0.f), part[j]);
-      }
+        for (int r = 0; r < 4; ++r) part[j] = fmaf(f.w[j][rb][r], relu(acc[j][rb][r]), part[j]);
     }
   }
   // Sum over the four 16-lane rows (head groups) and pack the 4 queries.
@@ -95,9 +112,23 @@ __device__ __forceinline__ float score_subtile(const QueryFrags<T, DI, NQ>& f,
   return (x + y) + 0.f;         // rows 0..3 -> queries 0, 2, 1, 3; "+0" turns -0 into +0
 }
 
+// Launch shape of the prefill kernel: waves per workgroup (4 queries each),
+// keys per LDS tile and keys per workgroup.
+#ifndef DSA_IDX_WAVES
+#define DSA_IDX_WAVES 8
+#endif
+#ifndef DSA_IDX_KT
+#define DSA_IDX_KT 64
+#endif
+#ifndef DSA_IDX_CHUNK
+#define DSA_IDX_CHUNK 2048
+#endif
+constexpr int kIdxWaves = DSA_IDX_WAVES, kIdxKT = DSA_IDX_KT, kIdxChunk = DSA_IDX_CHUNK;
+static_assert(kIdxChunk % kIdxKT == 0 && kIdxKT % 16 == 0, "key chunk is whole tiles of 16-key subtiles");
+
 template <typename T, int DI>
-__global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams a) {
-  constexpr int NT = 512, QT = 8 * QPW, KT = 64, KSTEPS = DI / 32;
+__global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a) {
+  constexpr int NT = 64 * kIdxWaves, QT = kIdxWaves * QPW, KT = kIdxKT, KSTEPS = DI / 32;
   constexpr int ROWB = DI * (int)sizeof(T), PITCH = ROWB + 16, CH16 = ROWB / 16;
   constexpr int TOT16 = KT * CH16, N16 = (TOT16 + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * KT * PITCH];
@@ -118,7 +149,6 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams a) {
     const int p_wave_last = a.q_pos0 + t_wave + nq - 1;
     QueryFrags<T, DI, QPW> f;
     load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
-    const bool two_rb = a.HI > 16;
     const int jl = ((g & 1) << 1) | (g >> 1);
     const int t_mine = t_wave + jl;
     const int p_mine = a.q_pos0 + t_mine;
@@ -156,23 +186,40 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams a) {
       const int buf = it & 1;
       if (it + 1 < n_tiles) gload(it + 1);
       const int s_tile = s_begin + it * KT;
+      auto load_b = [&](int sub, frag_t<T> (&bf)[KSTEPS]) {
+        const unsigned char* rowp = lds + buf * KT * PITCH + (sub * 16 + c) * PITCH;
 #pragma unroll
-      for (int sub = 0; sub < KT / 16; ++sub) {
-        const int s_sub = s_tile + sub * 16;
-        const int s = s_sub + c;
-        if (nq > 0 && s_sub <= p_wave_last) {
-          frag_t<T> bf[KSTEPS];
-          const unsigned char* rowp = lds + buf * KT * PITCH + (sub * 16 + c) * PITCH;
+        for (int kk = 0; kk < KSTEPS; ++kk)
+          bf[kk] = load_frag<T>(reinterpret_cast<const T*>(rowp + (32 * kk + 8 * g) * (int)sizeof(T)));
+      };
+      auto store = [&](int s, float e) {
+        if (t_mine < a.T) {
+          if (s <= p_mine) srow[s] = e;
+          else if (a.write_upper) srow[s] = ninf;
+        }
+      };
+      if (nq > 0 && s_tile + KT - 1 <= p_wave_last) {
+        // Whole tile below the wave's last query: the next subtile's key
+        // fragments are read from LDS while this one's MFMAs run.
+        frag_t<T> bf[2][KSTEPS];
+        load_b(0, bf[0]);
 #pragma unroll
-          for (int kk = 0; kk < KSTEPS; ++kk)
-            bf[kk] = load_frag<T>(reinterpret_cast<const T*>(rowp + (32 * kk + 8 * g) * (int)sizeof(T)));
-          const float e = score_subtile<T, DI, QPW>(f, bf, nq, two_rb);
-          if (t_mine < a.T) {
-            if (s <= p_mine) srow[s] = e;
-            else if (a.write_upper) srow[s] = ninf;
+        for (int sub = 0; sub < KT / 16; ++sub) {
+          if (sub + 1 < KT / 16) load_b(sub + 1, bf[(sub + 1) & 1]);
+          store(s_tile + sub * 16 + c, score_subtile<T, DI, QPW>(f, bf[sub & 1]));
+        }
+      } else {
+#pragma unroll
+        for (int sub = 0; sub < KT / 16; ++sub) {
+          const int s_sub = s_tile + sub * 16;
+          const int s = s_sub + c;
+          if (nq > 0 && s_sub <= p_wave_last) {
+            frag_t<T> bf[KSTEPS];
+            load_b(sub, bf);
+            store(s, score_subtile<T, DI, QPW>(f, bf));
+          } else if (a.write_upper && t_mine < a.T) {
+            srow[s] = ninf;
           }
-        } else if (a.write_upper && t_mine < a.T) {
-          srow[s] = ninf;
         }
       }
       if (it + 1 < n_tiles) lstore(buf ^ 1);
@@ -181,9 +228,11 @@ __global__ __launch_bounds__(512) void indexer_prefill_kernel(IndexerParams a) {
     s_filled = s_begin + n_tiles * KT;
   }
   if (a.write_upper && s_filled < s_chunk_end) {
-    const int ncol = s_chunk_end - s_filled, nrow = t_end - t0;
-    for (int i = tid; i < nrow * ncol; i += NT)
-      scores_b[(size_t)(t0 + i / ncol) * a.Lpad + s_filled + i % ncol] = ninf;
+    // rows t0..t_end-1, columns s_filled..s_chunk_end-1 (a multiple of 16): one
+    // wave per row, 4 floats per lane
+    for (int t = t0 + wave; t < t_end; t += NT / 64)
+      for (int s4 = s_filled + 4 * lane; s4 < s_chunk_end; s4 += 256)
+        *reinterpret_cast<f32x4*>(scores_b + (size_t)t * a.Lpad + s4) = f32x4{ninf, ninf, ninf, ninf};
   }
 }
 
@@ -209,7 +258,6 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
   if (s_begin < s_stop) {
     QueryFrags<T, DI, NQ> f;
     load_queries<T, DI, NQ>(f, a, b, t_first, c, g);
-    const bool two_rb = a.HI > 16;
     const T* kb = static_cast<const T*>(a.kidx) + (size_t)b * a.kv_cap * DI;
     const int n_sub = (s_stop - s_begin + 15) / 16;
     auto load_b = [&](int sub, frag_t<T> (&bf)[KSTEPS]) {
@@ -220,7 +268,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
         bf[kk] = sv ? load_frag<T>(kb + (size_t)s * DI + 32 * kk + 8 * g) : zero_frag<T>();
     };
     auto emit = [&](int sub, const frag_t<T> (&bf)[KSTEPS]) {
-      const float e = score_subtile<T, DI, NQ>(f, bf, nq, two_rb);
+      const float e = score_subtile<T, DI, NQ>(f, bf);
       const int s = s_begin + sub * 16 + c;
       if (t_mine < a.T) {
         if (s <= p_mine) srow[s] = e;
@@ -258,9 +306,9 @@ hipError_t launch_indexer_t(const IndexerParams& p, hipStream_t st) {
     dim3 grid((p.Lpad + q.key_chunk - 1) / q.key_chunk, (p.T + QPW - 1) / QPW, p.B);
     hipLaunchKernelGGL((indexer_decode_kernel<T, DI, QPW>), grid, dim3(256), 0, st, q);
   } else {
-    q.key_chunk = 512;
-    dim3 grid((p.Lpad + q.key_chunk - 1) / q.key_chunk, (p.T + 8 * QPW - 1) / (8 * QPW), p.B);
-    hipLaunchKernelGGL((indexer_prefill_kernel<T, DI>), grid, dim3(512), 0, st, q);
+    q.key_chunk = kIdxChunk;
+    dim3 grid((p.Lpad + q.key_chunk - 1) / q.key_chunk, (p.T + kIdxWaves * QPW - 1) / (kIdxWaves * QPW), p.B);
+    hipLaunchKernelGGL((indexer_prefill_kernel<T, DI>), grid, dim3(64 * kIdxWaves), 0, st, q);
   }
   return hipGetLastError();
 }
