@@ -58,7 +58,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle timing on the host (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one plain device copy of 1 GiB (reference for HBM counters)")
+                    help="also run one plain 1 GiB read + 1 GiB write kernel (reference for HBM counters)")
     ap.add_argument("--json-out", default=None, help="also write the JSON line to this file")
     return ap.parse_args()
 
@@ -294,16 +294,17 @@ def main():
         secondary.append({
             "workload": name, "value": r["value"], "unit": "queries/s",
             "ms_per_step": round(r["ms_per_step"], 4), "steps": args.secondary_steps,
-            "roofline": _roofline(r["dominant"]), "kernels": r["kernels"],
+            "roofline": _roofline(r["dominant"], name), "kernels": r["kernels"],
         })
     if args.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        # one plain streaming kernel of known size (2^28 float32: 1 GiB read,
+        # 1 GiB written) as the reference reading for the HBM byte counters
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 1 GiB read + 1 GiB written by one device copy")
+        log("[bench] copy calibration: torch.neg over 2^28 float32 (1 GiB read + 1 GiB written)")
         del src, dst
     cpu = None
     if args.cpu_seconds > 0:
@@ -327,7 +328,7 @@ def main():
             "top_k": wl.top_k, "attention": f"{wl.heads}x{wl.head_dim}", "kv_heads": wl.kv_heads,
             "tokens_per_s": head["value"],
         },
-        "roofline": _roofline(head["dominant"]),
+        "roofline": _roofline(head["dominant"], wl.name),
         "cpu_baseline": cpu,
         "kernels": head["kernels"],
         "secondary": secondary,
@@ -340,9 +341,38 @@ def main():
     print(text, flush=True)
 
 
-def _roofline(k):
+def kernel_sources_digest():
+    """sha256 over the library's kernel and host sources: traffic figures
+    taken from counters are reported only while the kernels are unchanged."""
+    import hashlib
+    d = os.path.join(ROOT, "dsa_lightning_indexer_03_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, op):
+    """HBM bytes per launch of `op` on `workload` from profiles/traffic.json
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE passes, scaled by the calibration
+    kernel's readings), or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = table.get("entries", {}).get(workload, {}).get(op)
+    if not ent or table.get("sources_sha256") != kernel_sources_digest():
+        return None
+    return 1024.0 * (ent["fetch_kib"] * table["fetch_scale"] + ent["write_kib"] * table["write_scale"])
+
+
+def _roofline(k, workload=None):
     return {"bound": k["bound"], "achieved": k["achieved"], "peak": k["peak"], "unit": k["unit"],
-            "frac": k["frac"], "traffic": None, "kernel": k["op"]}
+            "frac": k["frac"], "traffic": measured_traffic(workload, k["op"]), "kernel": k["op"]}
 
 
 if __name__ == "__main__":
