@@ -21,11 +21,14 @@
 //   S^T = K Q^T   A = K rows from LDS, B = Q^T; lane (c, g) ends up holding
 //                 keys 16*kb + 4*g + r (r = 0..3) of query c.
 //   O^T += V^T P^T  the S^T accumulators, exponentiated and rounded to bf16,
-//                 are used in place as the B operand; V^T is stored in LDS so
-//                 that the 8 keys a lane feeds per k-step are contiguous.
-// V is transposed in registers on its way into LDS (4 keys x 8 dims per
-// thread, byte permutes), and the V^T rows are XOR-swizzled in 16-byte units
-// so both the transposing writes and the fragment reads avoid bank conflicts.
+//                 are used in place as the B operand.
+// K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes per
+// lane, no registers), row-major with each row's 16-byte columns XOR-swizzled
+// by (row mod 16). The V^T operand of P V is read from the row-major V tile
+// with LDS transpose reads (ds_read_b64_tr_b16): within a 16-lane group, lane
+// c receives element c % 4 of the 8-byte pieces lanes 4k + c/4 point at, so
+// pointing lane 4r + j at dims 4j..4j+3 of key r gives each lane one dim of
+// four consecutive keys.
 //
 // Softmax. Scores are masked with one sign-extending bit extract and one
 // bitfield insert per element, exponentiated with exp2 against a running
@@ -48,10 +51,9 @@ constexpr int kD = 128;             // head dim
 constexpr int kKT = 64;             // keys per tile
 constexpr int kKS = kD / 32;        // k-steps of S^T (head dim / 32)
 constexpr int kDB = kD / 16;        // 16-dim blocks of O^T
-constexpr int kKPitch = kD * 2 + 16;         // bytes per K row in LDS (padded)
-constexpr int kKBytes = kKT * kKPitch;
-constexpr int kVBytes = kD * kKT * 2;        // V^T: kD rows of 64 keys, 128 B each
-constexpr int kStage = kKBytes + kVBytes;
+constexpr int kRow = kD * 2;                 // bytes per key row in LDS (K and V)
+constexpr int kTileBytes = kKT * kRow;       // one 64-key tile of K or V
+constexpr int kStage = 2 * kTileBytes;       // K tile then V tile
 constexpr float kLazyMax = 8.0f;             // log2 units
 constexpr float kLn2f = 0.69314718055994530942f;
 
@@ -59,14 +61,12 @@ constexpr int kQB = 2;               // 16-query blocks per wave
 constexpr int kQW = 16 * kQB;        // queries per wave
 constexpr int kQT = 4 * kQW;        // queries per workgroup
 
-// 16-byte column of V^T row d that holds logical column `chunk` (0..7).
-__device__ __forceinline__ int vt_chunk(int d, int chunk) { return chunk ^ ((d ^ (d >> 3)) & 7); }
+// Byte offset of 16-byte column `col` of key row `row` in a swizzled tile.
+__device__ __forceinline__ int tile_off(int row, int col) { return row * kRow + ((col ^ (row & 15)) << 4); }
 
-// Logical V^T column (16-B unit, 0..7) and 8-byte half of the 4 keys 4*kq..4*kq+3.
-// The PV k-step ks covers keys 32*ks + 16*hf + 4*g + r; lane group g reads
-// column 4*ks + g, whose two halves are hf = 0 and hf = 1.
-__device__ __forceinline__ int vt_col_of_quad(int kq) { return 4 * (kq >> 3) + (kq & 3); }
-__device__ __forceinline__ int vt_half_of_quad(int kq) { return (kq >> 2) & 1; }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ float mask_elem(float s, uint32_t word, int bit) {
   // all-ones when bit `bit` of word is set, else zero; then keep s or -inf
@@ -135,57 +135,21 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
     l_run[qb] = 0.f;
   }
 
-  // Tile loaders. K: 1024 16-B chunks, 4 per thread (chunk i = tid + 256 n:
-  // key i / 16, column i % 16). V: thread (kq = tid / 16, dc = tid % 16)
-  // loads dims 8*dc..8*dc+7 of keys 4*kq..4*kq+3. Keys past n_kv (last tile
-  // only) read the last cached row instead: finite data the mask gives zero
-  // weight.
-  const int v_kq = tid >> 4, v_dc = tid & 15;
-  const size_t tile_stride = (size_t)kKT * kv_tok;
-  const bf16* kp = kbase + (size_t)(tid >> 4) * kv_tok + (tid & 15) * 8;  // + 16 keys per n
-  const bf16* vp = vbase + (size_t)(4 * v_kq) * kv_tok + v_dc * 8;         // + 1 key per j
-  u32x4 kst[4], vst[4];
-  auto gload = [&](int tile) {
+  // Tile loader: wave w fills key rows 16w..16w+15 of the K and V tiles, four
+  // rows (1 KiB) per instruction; lane l writes physical column l % 16 of
+  // row l / 16, so it fetches the logical column that the swizzle puts
+  // there. Keys past n_kv (last tile only) read the last cached row instead:
+  // finite data the mask gives zero weight.
+  auto dload = [&](int tile, int buf) {
     const int s0 = tile * kKT;
-    if (s0 + kKT <= a.n_kv) {
-      const bf16* kt = kp + tile * tile_stride;
-      const bf16* vt = vp + tile * tile_stride;
-#pragma unroll
-      for (int n = 0; n < 4; ++n) kst[n] = *reinterpret_cast<const u32x4*>(kt + (size_t)(16 * n) * kv_tok);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vst[j] = *reinterpret_cast<const u32x4*>(vt + (size_t)j * kv_tok);
-    } else {
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int s = min(s0 + (tid >> 4) + 16 * n, a.n_kv - 1);
-        kst[n] = *reinterpret_cast<const u32x4*>(kbase + (size_t)s * kv_tok + (tid & 15) * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int s = min(s0 + 4 * v_kq + j, a.n_kv - 1);
-        vst[j] = *reinterpret_cast<const u32x4*>(vbase + (size_t)s * kv_tok + v_dc * 8);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* kl = lds + buf * kStage;
-    unsigned char* vl = kl + kKBytes;
+    unsigned char* st = lds + buf * kStage;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-      const int i = tid + n * 256, key = i >> 4, ch = i & 15;
-      *reinterpret_cast<u32x4*>(kl + key * kKPitch + ch * 16) = kst[n];
-    }
-    const int col = vt_col_of_quad(v_kq), half = vt_half_of_quad(v_kq);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      // dims 8*dc + 2m (low halves) and 8*dc + 2m + 1 (high halves) of the 4 keys
-      const uint32_t lo01 = __builtin_amdgcn_perm(vst[1][m], vst[0][m], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(vst[3][m], vst[2][m], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(vst[1][m], vst[0][m], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(vst[3][m], vst[2][m], 0x07060302u);
-      const int d0 = 8 * v_dc + 2 * m, d1 = d0 + 1;
-      *reinterpret_cast<uint2*>(vl + d0 * 128 + vt_chunk(d0, col) * 16 + half * 8) = make_uint2(lo01, lo23);
-      *reinterpret_cast<uint2*>(vl + d1 * 128 + vt_chunk(d1, col) * 16 + half * 8) = make_uint2(hi01, hi23);
+      const int r0 = 16 * wave + 4 * n, row = r0 + (lane >> 4);
+      const int col = (lane & 15) ^ (row & 15);
+      const size_t off = (size_t)min(s0 + row, a.n_kv - 1) * kv_tok + col * 8;
+      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(st + r0 * kRow), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(st + kTileBytes + r0 * kRow), 16, 0, 0);
     }
   };
 
@@ -198,9 +162,9 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   };
 
   const float sl2 = a.scale_log2;
-  gload(0);
+  dload(0, 0);
   mload(0);
-  lstore(0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
     const int buf = it & 1;
@@ -208,17 +172,17 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) mw[qb] = mw_next[qb];
     if (it + 1 < n_tiles) {
-      gload(it + 1);
+      dload(it + 1, buf ^ 1);
       mload(it + 1);
     }
     const int s0 = it * kKT;
     const unsigned char* kl = lds + buf * kStage;
-    const unsigned char* vl = kl + kKBytes;
+    const unsigned char* vl = kl + kTileBytes;
 
     if (wave_live && s0 <= pw_last) {
       // Causal limit folded into the mask words on diagonal tiles.
       const bool diag = s0 + kKT - 1 > pw_first;
-      bool any = false;
+      bool any = false, full = !diag;
 #pragma unroll
       for (int qb = 0; qb < kQB; ++qb) {
         uint32_t lo = mw[qb].x, hi = mw[qb].y;
@@ -232,6 +196,7 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
         if (tq[qb] >= a.T) lo = hi = 0u;
         mw[qb] = make_uint2(lo, hi);
         any = any || (lo | hi) != 0u;
+        full = full && (lo & hi) == 0xffffffffu;
       }
       if (ballot64(any) != 0ull) {
         // S^T = K Q^T
@@ -244,29 +209,46 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
         for (int kk = 0; kk < kKS; ++kk) {
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + (16 * kb + c) * kKPitch + (4 * kk + g) * 16);
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + tile_off(16 * kb + c, 4 * kk + g));
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = mma_kstep(kf, qreg[qb][kk], sacc[kb][qb]);
           }
         }
-        // Masked maxima; the running maximum is raised lazily.
-        bool need_any = false;
+        // Masked maxima (no masking when every query of the wave keeps the
+        // whole tile); the running maximum is raised lazily.
+        const bool plain = ballot64(!full) == 0ull;
         float mx_all[kQB];
+        if (plain) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) {
+            float mx = fneg_inf();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
+            mx_all[qb] = mx;
+          }
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) {
+            const uint32_t wlo = mw[qb].x >> (4 * g), whi = mw[qb].y >> (4 * g);
+            float mx = fneg_inf();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float v = mask_elem(sacc[kb][qb][r], kb < 2 ? wlo : whi, 16 * (kb & 1) + r);
+                sacc[kb][qb][r] = v;
+                mx = fmaxf(mx, v);
+              }
+            mx_all[qb] = mx;
+          }
+        }
+        bool need_any = false;
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
-          const uint32_t wlo = mw[qb].x >> (4 * g), whi = mw[qb].y >> (4 * g);
-          float mx = fneg_inf();
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float v = mask_elem(sacc[kb][qb][r], kb < 2 ? wlo : whi, 16 * (kb & 1) + r);
-              sacc[kb][qb][r] = v;
-              mx = fmaxf(mx, v);
-            }
-          mx = rows4_max(mx) * sl2;
-          mx_all[qb] = mx;
-          need_any = need_any || mx > m_run[qb] + kLazyMax;
+          mx_all[qb] = rows4_max(mx_all[qb]) * sl2;
+          need_any = need_any || mx_all[qb] > m_run[qb] + kLazyMax;
         }
         if (ballot64(need_any) != 0ull) {
 #pragma unroll
@@ -301,14 +283,23 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
-            const int d = 16 * db + c;
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vl + d * 128 + vt_chunk(d, 4 * ks + g) * 16);
+            // keys 32*ks + 16*hf + 4*g + (0..3), dim 16*db + c, for hf = 0, 1
+            v4i16 t[2];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              const int row = 32 * ks + 16 * hf + 4 * g + (c >> 2), j = c & 3;
+              t[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (lds_v4i16*)(vl + tile_off(row, 2 * db + (j >> 1)) + 8 * (j & 1)));
+            }
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) o[db][qb] = mma_kstep(vf, pf[qb][ks], o[db][qb]);
           }
       }
     }
-    if (it + 1 < n_tiles) lstore(buf ^ 1);
+    // the next tile's direct loads (and mask words) have landed in this
+    // wave; the barrier makes every wave's share visible
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
