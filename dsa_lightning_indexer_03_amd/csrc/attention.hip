@@ -323,7 +323,10 @@ __global__ __launch_bounds__(256) void attn_gather_partial_kernel(GatherParams a
   const int start = split * SPLIT;
   if (start >= count) return;
   const int ntok = min(SPLIT, count - start);
-  for (int i = tid; i < ntok; i += 256) tok[i] = a.list[(size_t)row * a.list_stride + start + i];
+  // Kept-token lists come from the library's own top-k or mask compaction and
+  // hold tokens in [0, n_kv); the clamp only guarantees that a corrupted list
+  // can never address memory outside the caches.
+  for (int i = tid; i < ntok; i += 256) tok[i] = min(max(a.list[(size_t)row * a.list_stride + start + i], 0), a.n_kv - 1);
   __syncthreads();
 
   const int group = a.H / a.Hkv;

@@ -24,7 +24,7 @@
 //                 are used in place as the B operand.
 // K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes per
 // lane, no registers), row-major with each row's 16-byte columns XOR-swizzled
-// by (row mod 16). The V^T operand of P V is read from the row-major V tile
+// (see swz) so that both operand reads are free of bank conflicts. The V^T operand of P V is read from the row-major V tile
 // with LDS transpose reads (ds_read_b64_tr_b16): within a 16-lane group, lane
 // c receives element c % 4 of the 8-byte pieces lanes 4k + c/4 point at, so
 // pointing lane 4r + j at dims 4j..4j+3 of key r gives each lane one dim of
@@ -61,8 +61,14 @@ constexpr int kQB = 2;               // 16-query blocks per wave
 constexpr int kQW = 16 * kQB;        // queries per wave
 constexpr int kQT = 4 * kQW;        // queries per workgroup
 
+// Swizzle of a key row's 16-byte columns: physical column = col ^ swz(row).
+// swz is a bijection on row mod 16 (so the 16 rows a K fragment read touches
+// land in 16 different columns) and, within every aligned group of four
+// rows, differs in its upper three bits (so the four rows x two columns a
+// 16-lane transpose read touches land in eight different columns).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
 // Byte offset of 16-byte column `col` of key row `row` in a swizzled tile.
-__device__ __forceinline__ int tile_off(int row, int col) { return row * kRow + ((col ^ (row & 15)) << 4); }
+__device__ __forceinline__ int tile_off(int row, int col) { return row * kRow + ((col ^ swz(row)) << 4); }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -140,16 +146,33 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   // row l / 16, so it fetches the logical column that the swizzle puts
   // there. Keys past n_kv (last tile only) read the last cached row instead:
   // finite data the mask gives zero weight.
+  int dl_row[4], dl_col[4];  // row of the tile and logical column this lane fetches, per instruction
+  uint32_t dl_off[4];        // element offset of that row/column from the tile's first key
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    dl_row[n] = 16 * wave + 4 * n + (lane >> 4);
+    dl_col[n] = (lane & 15) ^ swz(dl_row[n]);
+    dl_off[n] = (uint32_t)(dl_row[n] * kv_tok + dl_col[n] * 8);
+  }
   auto dload = [&](int tile, int buf) {
     const int s0 = tile * kKT;
     unsigned char* st = lds + buf * kStage;
+    const size_t tbase = (size_t)s0 * kv_tok;
+    if (s0 + kKT <= a.n_kv) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int r0 = 16 * wave + 4 * n, row = r0 + (lane >> 4);
-      const int col = (lane & 15) ^ (row & 15);
-      const size_t off = (size_t)min(s0 + row, a.n_kv - 1) * kv_tok + col * 8;
-      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(st + r0 * kRow), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(st + kTileBytes + r0 * kRow), 16, 0, 0);
+      for (int n = 0; n < 4; ++n) {
+        const int r0 = 16 * wave + 4 * n;
+        __builtin_amdgcn_global_load_lds(kbase + tbase + dl_off[n], (lds_void*)(st + r0 * kRow), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + tbase + dl_off[n], (lds_void*)(st + kTileBytes + r0 * kRow), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const int r0 = 16 * wave + 4 * n;
+        const size_t off = (size_t)min(s0 + dl_row[n], a.n_kv - 1) * kv_tok + dl_col[n] * 8;
+        __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(st + r0 * kRow), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(st + kTileBytes + r0 * kRow), 16, 0, 0);
+      }
     }
   };
 

@@ -21,6 +21,8 @@
 //  - indexer_decode_kernel: few queries per sequence; each wave streams its
 //    own 16-key subtiles straight from HBM into MFMA operands (every key is
 //    used once per query group, so LDS staging would only add traffic).
+#include <algorithm>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -42,6 +44,8 @@ struct QueryFrags {
 };
 
 // Loads the A fragments and head weights of queries t_first .. t_first+NQ-1.
+// Queries past T and heads past H_I read a valid row (finite data) and get
+// weight 0, so they add exact zeros; the loads carry no branches.
 template <typename T, int DI, int NQ>
 __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const IndexerParams& a, int b,
                                              int t_first, int c, int g) {
@@ -51,18 +55,27 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
   for (int j = 0; j < NQ; ++j) {
     const int t = t_first + j;
     const bool tv = t < a.T;
+    const int tc = min(t, a.T - 1);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int head = 16 * rb + c;
-      const bool hv = tv && head < a.HI;
+      const int head = min(16 * rb + c, a.HI - 1);
 #pragma unroll
       for (int kk = 0; kk < QueryFrags<T, DI, NQ>::KSTEPS; ++kk)
-        f.a[j][rb][kk] = hv ? load_frag<T>(qb + ((size_t)t * a.HI + head) * DI + 32 * kk + 8 * g)
-                            : zero_frag<T>();
+        f.a[j][rb][kk] = load_frag<T>(qb + ((size_t)tc * a.HI + head) * DI + 32 * kk + 8 * g);
+      // weights of heads 16*rb + 4*g + (0..3): one 16-byte load when H_I is a
+      // multiple of 4 (the row stays 16-byte aligned), else four scalar loads
+      const int h4 = 16 * rb + 4 * g;
+      if ((a.HI & 3) == 0) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(wb + (size_t)tc * a.HI + min(h4, a.HI - 4));
+        const float keep = (tv && h4 < a.HI) ? 1.f : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int h2 = 16 * rb + 4 * g + r;
-        f.w[j][rb][r] = (tv && h2 < a.HI) ? wb[(size_t)t * a.HI + h2] : 0.f;
+        for (int r = 0; r < 4; ++r) f.w[j][rb][r] = wv[r] * keep;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float wv = wb[(size_t)tc * a.HI + min(h4 + r, a.HI - 1)];
+          f.w[j][rb][r] = wv * ((tv && h4 + r < a.HI) ? 1.f : 0.f);
+        }
       }
     }
   }
@@ -112,128 +125,188 @@ __device__ __forceinline__ float score_subtile(const QueryFrags<T, DI, NQ>& f,
   return (x + y) + 0.f;         // rows 0..3 -> queries 0, 2, 1, 3; "+0" turns -0 into +0
 }
 
-// Launch shape of the prefill kernel: waves per workgroup (4 queries each),
-// keys per LDS tile and keys per workgroup.
+// Prefill work is cut into units (sequence b, 32-query tile qt, 64-key tile
+// kt), kt covering keys 0..p_last of the query tile, ordered b, qt, kt. A
+// fixed grid of workgroups (one per CU) takes equal contiguous ranges of
+// units, so every CU gets the same amount of matrix work whatever the causal
+// shape, and a workgroup reloads its queries' q fragments only when its range
+// crosses into the next query tile.
 #ifndef DSA_IDX_WAVES
 #define DSA_IDX_WAVES 8
 #endif
-#ifndef DSA_IDX_KT
-#define DSA_IDX_KT 64
+#ifndef DSA_IDX_WG_PER_CU
+#define DSA_IDX_WG_PER_CU 1
 #endif
-#ifndef DSA_IDX_CHUNK
-#define DSA_IDX_CHUNK 2048
-#endif
-constexpr int kIdxWaves = DSA_IDX_WAVES, kIdxKT = DSA_IDX_KT, kIdxChunk = DSA_IDX_CHUNK;
-static_assert(kIdxChunk % kIdxKT == 0 && kIdxKT % 16 == 0, "key chunk is whole tiles of 16-key subtiles");
+constexpr int kIdxWaves = DSA_IDX_WAVES;      // waves per workgroup, 4 queries each
+constexpr int kIdxQT = kIdxWaves * QPW;      // 32 queries per query tile
+constexpr int kIdxKT = 64;                    // keys per key tile
+static_assert(kIdxKT % kIdxQT == 0, "query tile divides key tile");
+
+struct UnitMap {
+  int T, q_pos0, nqt, nfull;
+  long long per_seq;
+  __device__ __host__ int ntk(int qt) const { return (q_pos0 + min(kIdxQT * qt + kIdxQT - 1, T - 1)) / kIdxKT + 1; }
+  // sum over x < n of floor(x / R), R = key tile / query tile
+  __device__ __host__ static long long floor_sum(long long n) {
+    constexpr int R = kIdxKT / kIdxQT;
+    const long long m = n / R;
+    return R * m * (m - 1) / 2 + (n - R * m) * m;
+  }
+  // units of query tiles 0..n-1. A full query tile qt has
+  // floor((A + QT qt) / KT) + 1 key tiles, A = q_pos0 + QT - 1; with
+  // A = a0 KT + rq QT + rr (rr < QT) that is a0 + 1 + floor((qt + rq) / R).
+  __device__ __host__ long long prefix(int n) const {
+    const int A = q_pos0 + kIdxQT - 1, a0 = A / kIdxKT, rq = (A % kIdxKT) / kIdxQT;
+    const long long k = min(n, nfull);
+    long long s = k * (a0 + 1) + floor_sum(rq + k) - floor_sum(rq);
+    if (n > nfull) s += ntk(nfull);
+    return s;
+  }
+  __device__ __host__ void init(int T_, int q_pos0_) {
+    T = T_;
+    q_pos0 = q_pos0_;
+    nqt = (T + kIdxQT - 1) / kIdxQT;
+    nfull = T / kIdxQT;
+    per_seq = prefix(nqt);
+  }
+  // (b, qt, kt) of unit u
+  __device__ void decode(long long u, int& b, int& qt, int& kt) const {
+    b = (int)(u / per_seq);
+    const long long v = u - (long long)b * per_seq;
+    int lo = 0, hi = nqt - 1;  // largest qt with prefix(qt) <= v
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix(mid) <= v) lo = mid;
+      else hi = mid - 1;
+    }
+    qt = lo;
+    kt = (int)(v - prefix(lo));
+  }
+};
 
 template <typename T, int DI>
-__global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a) {
-  constexpr int NT = 64 * kIdxWaves, QT = kIdxWaves * QPW, KT = kIdxKT, KSTEPS = DI / 32;
+__global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a, UnitMap um,
+                                                                          long long n_units) {
+  constexpr int NT = 64 * kIdxWaves, KT = kIdxKT, KSTEPS = DI / 32;
   constexpr int ROWB = DI * (int)sizeof(T), PITCH = ROWB + 16, CH16 = ROWB / 16;
   constexpr int TOT16 = KT * CH16, N16 = (TOT16 + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * KT * PITCH];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const int b = blockIdx.z, t0 = blockIdx.y * QT, s_begin = blockIdx.x * a.key_chunk;
-  const int t_end = min(t0 + QT, a.T);
-  const int p_last = a.q_pos0 + t_end - 1;
-  const int s_chunk_end = min(s_begin + a.key_chunk, a.Lpad);
-  const int s_stop = min(s_chunk_end, p_last + 1);
-  float* scores_b = a.scores + (size_t)b * a.T * a.Lpad;
+  const long long u0 = (long long)blockIdx.x * n_units / gridDim.x;
+  const long long u1 = (long long)(blockIdx.x + 1) * n_units / gridDim.x;
+  if (u0 >= u1) return;
   const float ninf = fneg_inf();
-  int s_filled = s_begin;
+  const int jl = ((g & 1) << 1) | (g >> 1);  // query of the wave whose score this lane ends up with
 
-  if (s_begin < s_stop) {
-    const int t_wave = t0 + wave * QPW;
-    const int nq = max(0, min(QPW, a.T - t_wave));
-    const int p_wave_last = a.q_pos0 + t_wave + nq - 1;
-    QueryFrags<T, DI, QPW> f;
-    load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
-    const int jl = ((g & 1) << 1) | (g >> 1);
-    const int t_mine = t_wave + jl;
-    const int p_mine = a.q_pos0 + t_mine;
-    float* srow = scores_b + (size_t)t_mine * a.Lpad;
-
+  // Key tiles of the range, staged through LDS (double-buffered): unit u's
+  // tile is loaded while unit u-1 is scored.
+  u32x4 stg[N16];
+  auto gload = [&](int b, int kt) {
     const T* kb = static_cast<const T*>(a.kidx) + (size_t)b * a.kv_cap * DI;
-    const int n_tiles = (s_stop - s_begin + KT - 1) / KT;
-    u32x4 stg[N16];
-    auto gload = [&](int tile) {
-      const int s0 = s_begin + tile * KT;
 #pragma unroll
-      for (int n = 0; n < N16; ++n) {
-        const int i = tid + n * NT;
-        if (i < TOT16) {
-          const int s = s0 + i / CH16;
-          stg[n] = s < a.n_kv ? *reinterpret_cast<const u32x4*>(
-                                    reinterpret_cast<const char*>(kb + (size_t)s * DI) + (i % CH16) * 16)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int n = 0; n < N16; ++n) {
+      const int i = tid + n * NT;
+      if (i < TOT16) {
+        const int s = min(kt * KT + i / CH16, a.n_kv - 1);  // keys past n_kv: a valid row, never stored
+        stg[n] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kb + (size_t)s * DI) + (i % CH16) * 16);
       }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int n = 0; n < N16; ++n) {
-        const int i = tid + n * NT;
-        if (i < TOT16)
-          *reinterpret_cast<u32x4*>(lds + buf * KT * PITCH + (i / CH16) * PITCH + (i % CH16) * 16) = stg[n];
-      }
-    };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int it = 0; it < n_tiles; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < n_tiles) gload(it + 1);
-      const int s_tile = s_begin + it * KT;
-      auto load_b = [&](int sub, frag_t<T> (&bf)[KSTEPS]) {
-        const unsigned char* rowp = lds + buf * KT * PITCH + (sub * 16 + c) * PITCH;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
-          bf[kk] = load_frag<T>(reinterpret_cast<const T*>(rowp + (32 * kk + 8 * g) * (int)sizeof(T)));
-      };
-      auto store = [&](int s, float e) {
-        if (t_mine < a.T) {
-          if (s <= p_mine) srow[s] = e;
-          else if (a.write_upper) srow[s] = ninf;
-        }
-      };
-      if (nq > 0 && s_tile + KT - 1 <= p_wave_last) {
-        // Whole tile below the wave's last query: the next subtile's key
-        // fragments are read from LDS while this one's MFMAs run.
-        frag_t<T> bf[2][KSTEPS];
-        load_b(0, bf[0]);
-#pragma unroll
-        for (int sub = 0; sub < KT / 16; ++sub) {
-          if (sub + 1 < KT / 16) load_b(sub + 1, bf[(sub + 1) & 1]);
-          store(s_tile + sub * 16 + c, score_subtile<T, DI, QPW>(f, bf[sub & 1]));
-        }
-      } else {
-#pragma unroll
-        for (int sub = 0; sub < KT / 16; ++sub) {
-          const int s_sub = s_tile + sub * 16;
-          const int s = s_sub + c;
-          if (nq > 0 && s_sub <= p_wave_last) {
-            frag_t<T> bf[KSTEPS];
-            load_b(sub, bf);
-            store(s, score_subtile<T, DI, QPW>(f, bf));
-          } else if (a.write_upper && t_mine < a.T) {
-            srow[s] = ninf;
-          }
-        }
-      }
-      if (it + 1 < n_tiles) lstore(buf ^ 1);
-      __syncthreads();
     }
-    s_filled = s_begin + n_tiles * KT;
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int n = 0; n < N16; ++n) {
+      const int i = tid + n * NT;
+      if (i < TOT16)
+        *reinterpret_cast<u32x4*>(lds + buf * KT * PITCH + (i / CH16) * PITCH + (i % CH16) * 16) = stg[n];
+    }
+  };
+
+  int b, qt, kt;
+  um.decode(u0, b, qt, kt);
+  gload(b, kt);
+  lstore(0);
+  __syncthreads();
+
+  QueryFrags<T, DI, QPW> f;
+  int cur_b = -1, cur_qt = -1;
+  int t_wave = 0, p_wave_last = -1, t_mine = 0, p_mine = 0;
+  float* srow = nullptr;
+  for (long long u = u0; u < u1; ++u) {
+    const int buf = (int)((u - u0) & 1);
+    // next unit
+    int nb = b, nqt = qt, nkt = kt + 1;
+    if (nkt == um.ntk(qt)) {
+      nkt = 0;
+      if (++nqt == um.nqt) {
+        nqt = 0;
+        ++nb;
+      }
+    }
+    if (u + 1 < u1) gload(nb, nkt);
+    if (b != cur_b || qt != cur_qt) {
+      cur_b = b;
+      cur_qt = qt;
+      t_wave = qt * kIdxQT + wave * QPW;
+      const int nq = max(0, min(QPW, a.T - t_wave));
+      p_wave_last = a.q_pos0 + t_wave + nq - 1;
+      load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
+      t_mine = t_wave + jl;
+      p_mine = a.q_pos0 + t_mine;
+      srow = a.scores + ((size_t)b * a.T + min(t_mine, a.T - 1)) * a.Lpad;
+    }
+    const int s_tile = kt * KT;
+    auto load_b = [&](int sub, frag_t<T> (&bf)[KSTEPS]) {
+      const unsigned char* rowp = lds + buf * KT * PITCH + (sub * 16 + c) * PITCH;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        bf[kk] = load_frag<T>(reinterpret_cast<const T*>(rowp + (32 * kk + 8 * g) * (int)sizeof(T)));
+    };
+    auto store = [&](int s, float e) {
+      if (t_mine < a.T) {
+        if (s <= p_mine) srow[s] = e;
+        else if (a.write_upper) srow[s] = ninf;
+      }
+    };
+    if (t_wave < a.T && s_tile + KT - 1 <= p_wave_last) {
+      // Whole tile below the wave's last query.
+#pragma unroll
+      for (int sub = 0; sub < KT / 16; ++sub) {
+        frag_t<T> bf[KSTEPS];
+        load_b(sub, bf);
+        store(s_tile + sub * 16 + c, score_subtile<T, DI, QPW>(f, bf));
+      }
+    } else if (t_wave < a.T) {
+#pragma unroll
+      for (int sub = 0; sub < KT / 16; ++sub) {
+        const int s_sub = s_tile + sub * 16;
+        if (s_sub <= p_wave_last) {
+          frag_t<T> bf[KSTEPS];
+          load_b(sub, bf);
+          store(s_sub + c, score_subtile<T, DI, QPW>(f, bf));
+        } else if (a.write_upper && t_mine < a.T) {
+          srow[s_sub + c] = ninf;
+        }
+      }
+    }
+    if (u + 1 < u1) lstore(buf ^ 1);
+    __syncthreads();
+    b = nb;
+    qt = nqt;
+    kt = nkt;
   }
-  if (a.write_upper && s_filled < s_chunk_end) {
-    // rows t0..t_end-1, columns s_filled..s_chunk_end-1 (a multiple of 16): one
-    // wave per row, 4 floats per lane
-    for (int t = t0 + wave; t < t_end; t += NT / 64)
-      for (int s4 = s_filled + 4 * lane; s4 < s_chunk_end; s4 += 256)
-        *reinterpret_cast<f32x4*>(scores_b + (size_t)t * a.Lpad + s4) = f32x4{ninf, ninf, ninf, ninf};
-  }
+}
+
+// -inf for the columns past each query tile's last key tile (scores rows of
+// index_scores are written in full; the prefill kernel writes key tiles
+// 0..ntk(qt)-1 only). One workgroup per query row.
+__global__ __launch_bounds__(256) void scores_upper_fill_kernel(IndexerParams a, UnitMap um) {
+  const int row = blockIdx.x, t = row % a.T;
+  const int s_from = um.ntk(t / kIdxQT) * kIdxKT;
+  float* srow = a.scores + (size_t)row * a.Lpad;
+  const float ninf = fneg_inf();
+  for (int s4 = s_from + 4 * threadIdx.x; s4 < a.Lpad; s4 += 4 * 256)
+    *reinterpret_cast<f32x4*>(srow + s4) = f32x4{ninf, ninf, ninf, ninf};
 }
 
 // Few queries per sequence: grid (key chunks, ceil(T/NQ), B), 4 waves; wave w
@@ -294,6 +367,19 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
   }
 }
 
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <typename T, int DI>
 hipError_t launch_indexer_t(const IndexerParams& p, hipStream_t st) {
   IndexerParams q = p;
@@ -306,9 +392,16 @@ hipError_t launch_indexer_t(const IndexerParams& p, hipStream_t st) {
     dim3 grid((p.Lpad + q.key_chunk - 1) / q.key_chunk, (p.T + QPW - 1) / QPW, p.B);
     hipLaunchKernelGGL((indexer_decode_kernel<T, DI, QPW>), grid, dim3(256), 0, st, q);
   } else {
-    q.key_chunk = kIdxChunk;
-    dim3 grid((p.Lpad + q.key_chunk - 1) / q.key_chunk, (p.T + kIdxWaves * QPW - 1) / (kIdxWaves * QPW), p.B);
-    hipLaunchKernelGGL((indexer_prefill_kernel<T, DI>), grid, dim3(64 * kIdxWaves), 0, st, q);
+    UnitMap um;
+    um.init(p.T, p.q_pos0);
+    const long long n_units = um.per_seq * p.B;
+    if (p.write_upper) {
+      hipLaunchKernelGGL(scores_upper_fill_kernel, dim3(p.B * p.T), dim3(256), 0, st, q, um);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const int n_wg = (int)std::min<long long>(n_units, (long long)device_cu_count() * DSA_IDX_WG_PER_CU);
+    hipLaunchKernelGGL((indexer_prefill_kernel<T, DI>), dim3(n_wg), dim3(64 * kIdxWaves), 0, st, q, um, n_units);
   }
   return hipGetLastError();
 }

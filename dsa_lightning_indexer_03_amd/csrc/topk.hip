@@ -39,7 +39,7 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* re
 template <int NW, int EPT_R, int EPT_L>
 __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
   constexpr int NT = NW * 64, EPT = EPT_R + EPT_L;
-  static_assert(EPT_L % 8 == 0, "LDS-held elements load 8 at a time");
+  static_assert(EPT_L % 16 == 0, "LDS-held elements load 16 at a time");
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t lkeys[EPT_L > 0 ? EPT_L * NT : 1];  // element e >= EPT_R of thread tid
   __shared__ uint32_t red[NW];
@@ -64,25 +64,32 @@ __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
     return;
   }
 
+  // Loads are unconditional (positions past the row read its last candidate,
+  // then become the "no token" key 0), so they all stay in flight together
+  // instead of each waiting behind a branch.
+  // The scheduling barriers keep each batch of loads together ahead of its
+  // conversions, which the scheduler would otherwise pair one by one.
   const int base = wave * EPT * 64;
+  auto to_key = [&](float v, int idx) -> uint32_t { return idx < n ? orderable_key(v) : 0u; };
   uint32_t rkey[EPT_R];
-  if (EPT_L > 0) {  // LDS-held elements first, 8 loads in flight at a time
+  if (EPT_L > 0) {  // LDS-held elements first, 16 loads in flight at a time
 #pragma unroll 1
-    for (int e0 = EPT_R; e0 < EPT; e0 += 8) {
-      uint32_t k8[8];
+    for (int e0 = EPT_R; e0 < EPT; e0 += 16) {
+      float v16[16];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int idx = base + (e0 + j) * 64 + lane;
-        k8[j] = idx < n ? orderable_key(srow[idx]) : 0u;
-      }
+      for (int j = 0; j < 16; ++j) v16[j] = srow[min(base + (e0 + j) * 64 + lane, n - 1)];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) lkeys[(e0 + j - EPT_R) * NT + tid] = k8[j];
+      for (int j = 0; j < 16; ++j) lkeys[(e0 + j - EPT_R) * NT + tid] = to_key(v16[j], base + (e0 + j) * 64 + lane);
     }
   }
+  {
+    float v[EPT_R];
 #pragma unroll
-  for (int e = 0; e < EPT_R; ++e) {
-    const int idx = base + e * 64 + lane;
-    rkey[e] = idx < n ? orderable_key(srow[idx]) : 0u;
+    for (int e = 0; e < EPT_R; ++e) v[e] = srow[min(base + e * 64 + lane, n - 1)];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int e = 0; e < EPT_R; ++e) rkey[e] = to_key(v[e], base + e * 64 + lane);
   }
   // e is a compile-time constant at every use, so this picks a register or LDS.
   auto key = [&](int e) -> uint32_t { return e < EPT_R ? rkey[e < EPT_R ? e : 0] : lkeys[(e - EPT_R) * NT + tid]; };
