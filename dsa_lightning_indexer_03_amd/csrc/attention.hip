@@ -19,11 +19,12 @@
 //   (workgroup id mod 8) so its L2 serves their shared K/V stream, and the
 //   longest query tiles are dispatched first.
 //
-// attn_gather_partial_kernel / attn_gather_combine_kernel - few queries per
-//   sequence (decode). Each workgroup takes up to 128 kept tokens of one
-//   query (a split), fetches their whole K/V rows (contiguous across heads),
-//   and writes a partial (max, sum, unnormalised output) per head; the
-//   combine kernel merges the splits. Kept tokens are read once per query.
+// attn_gather_kernel - few queries per sequence (decode). Each workgroup
+//   takes up to 128 kept tokens of one query (a split), streams their whole
+//   K/V rows (contiguous across heads) through a per-lane online softmax and
+//   writes a partial (max, sum, unnormalised output) per head;
+//   attn_gather_combine_kernel merges the partials. Kept tokens are read
+//   once per query.
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -309,20 +310,28 @@ template <> __device__ __forceinline__ void chunk_to_float<float>(const u32x4& v
   for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
 }
 
+// One workgroup per (query row, split of up to SPLIT kept tokens). Each lane
+// keeps an online softmax (running max in log2 units, sum, unnormalised
+// output) for the head chunk(s) it holds and streams the split's tokens U at
+// a time, with all of their K and V loads in flight together; token slots of
+// a wave (TPI > 1) are merged at the end, and the workgroup writes its
+// partial. A row with no kept token still gets split 0, which writes the
+// empty partial (max -inf, sum 0).
 template <typename T, int D, int HW>
-__global__ __launch_bounds__(256) void attn_gather_partial_kernel(GatherParams a) {
+__global__ __launch_bounds__(256) void attn_gather_kernel(GatherParams a) {
   using C = GatherCfg<T, D, HW>;
-  constexpr int SPLIT = C::SPLIT, EPC = C::EPC, CHH = C::CHH, TPI = C::TPI, NIT = C::NIT;
-  __shared__ float sp[4][SPLIT][HW];  // scores, then probabilities, per wave
+  constexpr int SPLIT = C::SPLIT, EPC = C::EPC, CHH = C::CHH, TPI = C::TPI, NIT = C::NIT, U = kGatherUnroll;
+  constexpr int LPS = 64 / TPI;  // lanes per token slot
   __shared__ int tok[SPLIT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.y, split = blockIdx.x;
   const int b = row / a.T, t = row % a.T, p = a.q_pos0 + t;
   const int count = a.counts ? a.counts[row] : min(a.top_k, p + 1);
+  const int ns = max(1, (count + SPLIT - 1) / SPLIT);  // an empty row still gets one split
+  if (split >= ns) return;
   const int start = split * SPLIT;
-  if (start >= count) return;
-  const int ntok = min(SPLIT, count - start);
+  const int ntok = max(0, min(SPLIT, count - start));
   // Kept-token lists come from the library's own top-k or mask compaction and
   // hold tokens in [0, n_kv); the clamp only guarantees that a corrupted list
   // can never address memory outside the caches.
@@ -331,39 +340,47 @@ __global__ __launch_bounds__(256) void attn_gather_partial_kernel(GatherParams a
 
   const int group = a.H / a.Hkv;
   const int h0 = wave * HW;
-  // lane -> (token slot, chunk): chunk index cc in [0, NCHK) = head_local * CHH + part
-  const int tslot = lane / (64 / TPI > 0 ? 64 / TPI : 1);
-  const int lane_c = TPI > 1 ? lane % (64 / TPI) : lane;
+  const int tslot = lane / LPS, lane_c = lane % LPS;
   const size_t kv_tok = (size_t)a.Hkv * D;
   const T* kb = static_cast<const T*>(a.k) + (size_t)b * a.kv_cap * kv_tok;
   const T* vb = static_cast<const T*>(a.v) + (size_t)b * a.kv_cap * kv_tok;
 
-  // Query values of the chunks this lane handles, in float.
+  // Query values of the chunks this lane handles (in float), and the offsets
+  // of those chunks inside a token's K/V row.
   float qv[NIT][EPC];
+  size_t coff[NIT];
 #pragma unroll
   for (int it = 0; it < NIT; ++it) {
     const int cc = it * 64 + lane_c, hl = cc / CHH, part = cc % CHH;
     const T* qp = static_cast<const T*>(a.q) + (((size_t)b * a.T + t) * a.H + h0 + hl) * D + part * EPC;
     chunk_to_float<T>(*reinterpret_cast<const u32x4*>(qp), qv[it]);
+    coff[it] = (size_t)((h0 + hl) / group) * D + part * EPC;
   }
 
-  // Phase 1: scores (log2 units) of every kept token for the wave's heads.
-  for (int i0 = 0; i0 < ntok; i0 += TPI * 2) {
-    u32x4 kc[2][NIT];
+  float m[NIT], l[NIT], acc[NIT][EPC];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = i0 + u * TPI + tslot;
+  for (int it = 0; it < NIT; ++it) {
+    m[it] = fneg_inf();
+    l[it] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[it][e] = 0.f;
+  }
+
+  for (int i0 = 0; i0 < ntok; i0 += U * TPI) {
+    u32x4 kc[U][NIT], vc[U][NIT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const size_t off = (size_t)tok[min(i0 + u * TPI + tslot, ntok - 1)] * kv_tok;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const int cc = it * 64 + lane_c, hl = cc / CHH, part = cc % CHH;
-        kc[u][it] = i < ntok ? *reinterpret_cast<const u32x4*>(kb + (size_t)tok[i] * kv_tok +
-                                                               (size_t)((h0 + hl) / group) * D + part * EPC)
-                             : u32x4{0u, 0u, 0u, 0u};
+        kc[u][it] = *reinterpret_cast<const u32x4*>(kb + off + coff[it]);
+        vc[u][it] = *reinterpret_cast<const u32x4*>(vb + off + coff[it]);
       }
     }
+    float sc[U][NIT];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = i0 + u * TPI + tslot;
+    for (int u = 0; u < U; ++u) {
+      const bool valid = i0 + u * TPI + tslot < ntok;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
         float kf[EPC];
@@ -373,79 +390,49 @@ __global__ __launch_bounds__(256) void attn_gather_partial_kernel(GatherParams a
         for (int e = 0; e < EPC; ++e) d = fmaf(qv[it][e], kf[e], d);
 #pragma unroll
         for (int off = 1; off < CHH; off <<= 1) d += __shfl_xor(d, off, 64);
-        const int cc = it * 64 + lane_c, hl = cc / CHH, part = cc % CHH;
-        if (part == 0 && i < ntok) sp[wave][i][hl] = d * a.scale_log2;
-      }
-    }
-  }
-  __syncthreads();
-
-  // Phase 2: per-head max and sum over the split; probabilities in place.
-  float* part_ml = a.part_ml + ((size_t)row * a.n_splits + split) * a.H * 2;
-  for (int hl = 0; hl < HW; ++hl) {
-    float mx = fneg_inf();
-    for (int i = lane; i < ntok; i += 64) mx = fmaxf(mx, sp[wave][i][hl]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    float sum = 0.f;
-    for (int i = lane; i < ntok; i += 64) {
-      const float e = __builtin_amdgcn_exp2f(sp[wave][i][hl] - mx);
-      sp[wave][i][hl] = e;
-      sum += e;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
-    if (lane == 0) {
-      part_ml[2 * (h0 + hl)] = mx;
-      part_ml[2 * (h0 + hl) + 1] = sum;
-    }
-  }
-  __syncthreads();
-
-  // Phase 3: unnormalised P V for the wave's heads.
-  float acc[NIT][EPC];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[it][e] = 0.f;
-  for (int i0 = 0; i0 < ntok; i0 += TPI * 2) {
-    u32x4 vc[2][NIT];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = i0 + u * TPI + tslot;
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        const int cc = it * 64 + lane_c, hl = cc / CHH, part = cc % CHH;
-        vc[u][it] = i < ntok ? *reinterpret_cast<const u32x4*>(vb + (size_t)tok[i] * kv_tok +
-                                                               (size_t)((h0 + hl) / group) * D + part * EPC)
-                             : u32x4{0u, 0u, 0u, 0u};
+        sc[u][it] = valid ? d * a.scale_log2 : fneg_inf();
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = i0 + u * TPI + tslot;
-      if (i < ntok) {
+    for (int it = 0; it < NIT; ++it) {
+      float mx = m[it];
 #pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-          const int cc = it * 64 + lane_c, hl = cc / CHH;
-          const float pr = sp[wave][i][hl];
-          float vf[EPC];
-          chunk_to_float<T>(vc[u][it], vf);
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, sc[u][it]);
+      const float mref = mx == fneg_inf() ? 0.f : mx;  // no finite score yet: every weight is 0
+      const float alpha = __builtin_amdgcn_exp2f(m[it] - mref);
+      l[it] *= alpha;
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[it][e] = fmaf(pr, vf[e], acc[it][e]);
-        }
+      for (int e = 0; e < EPC; ++e) acc[it][e] *= alpha;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float pr = __builtin_amdgcn_exp2f(sc[u][it] - mref);
+        l[it] += pr;
+        float vf[EPC];
+        chunk_to_float<T>(vc[u][it], vf);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[it][e] = fmaf(pr, vf[e], acc[it][e]);
       }
+      m[it] = mx;
     }
   }
-  // Lanes that handled different token slots of the same chunk add up.
+  // Merge the token slots of the wave (lanes LPS apart hold the same chunk).
 #pragma unroll
-  for (int it = 0; it < NIT; ++it)
+  for (int off = LPS; off < 64; off <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e)
+    for (int it = 0; it < NIT; ++it) {
+      const float mo = __shfl_xor(m[it], off, 64), lo = __shfl_xor(l[it], off, 64);
+      const float mx = fmaxf(m[it], mo);
+      const float mref = mx == fneg_inf() ? 0.f : mx;
+      const float fa = __builtin_amdgcn_exp2f(m[it] - mref), fb = __builtin_amdgcn_exp2f(mo - mref);
+      l[it] = l[it] * fa + lo * fb;
 #pragma unroll
-      for (int off = 64 / TPI; off < 64; off <<= 1) acc[it][e] += __shfl_xor(acc[it][e], off, 64);
+      for (int e = 0; e < EPC; ++e) acc[it][e] = acc[it][e] * fa + __shfl_xor(acc[it][e], off, 64) * fb;
+      m[it] = mx;
+    }
+  }
   if (tslot == 0) {
     float* po = a.part_o + ((size_t)row * a.n_splits + split) * a.H * D;
+    float* pml = a.part_ml + ((size_t)row * a.n_splits + split) * a.H * 2;
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int cc = it * 64 + lane_c, hl = cc / CHH, part = cc % CHH;
@@ -453,25 +440,31 @@ __global__ __launch_bounds__(256) void attn_gather_partial_kernel(GatherParams a
 #pragma unroll
       for (int e = 0; e < EPC; e += 4)
         *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[it][e], acc[it][e + 1], acc[it][e + 2], acc[it][e + 3]};
+      if (part == 0) {
+        pml[2 * (h0 + hl)] = m[it];
+        pml[2 * (h0 + hl) + 1] = l[it];
+      }
     }
   }
 }
 
 // One workgroup per (head, query row), one thread per output dim: the split
-// partials of that head are merged by their log-sum-exp.
+// partials of that head are merged by their log-sum-exp. A row with no kept
+// token gets a zero output and lse = -inf.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_gather_combine_kernel(GatherParams a) {
   const int h = blockIdx.x, row = blockIdx.y, d = threadIdx.x;
   const int b = row / a.T, t = row % a.T, p = a.q_pos0 + t;
   const int count = a.counts ? a.counts[row] : min(a.top_k, p + 1);
-  const int ns = (count + kGatherSplit - 1) / kGatherSplit;
+  const int ns = max(1, (count + kGatherSplit - 1) / kGatherSplit);
   const float* ml = a.part_ml + (size_t)row * a.n_splits * a.H * 2 + 2 * h;
   const float* po = a.part_o + (size_t)row * a.n_splits * a.H * D + (size_t)h * D + d;
   float M = fneg_inf();
   for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[(size_t)j * a.H * 2]);
+  const float Mr = M == fneg_inf() ? 0.f : M;
   float L = 0.f, O = 0.f;
   for (int j = 0; j < ns; ++j) {
-    const float f = __builtin_amdgcn_exp2f(ml[(size_t)j * a.H * 2] - M);
+    const float f = __builtin_amdgcn_exp2f(ml[(size_t)j * a.H * 2] - Mr);
     L += f * ml[(size_t)j * a.H * 2 + 1];
     O += f * po[(size_t)j * a.H * D];
   }
@@ -526,7 +519,7 @@ hipError_t launch_prefill_t(const AttnParams& p, hipStream_t st) {
 
 template <typename T, int D, int HW>
 hipError_t launch_gather_hw(const GatherParams& p, hipStream_t st) {
-  hipLaunchKernelGGL((attn_gather_partial_kernel<T, D, HW>), dim3(p.n_splits, p.B * p.T), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((attn_gather_kernel<T, D, HW>), dim3(p.n_splits, p.B * p.T), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((attn_gather_combine_kernel<T, D>), dim3(p.H, p.B * p.T), dim3(D), 0, st, p);

@@ -59,7 +59,14 @@ struct GatherParams {
   int B, T, q_pos0, n_kv, kv_cap, H, Hkv, n_splits;
   float scale_log2;
 };
-constexpr int kGatherSplit = 128;  // kept tokens per split workgroup
+#ifndef DSA_GATHER_SPLIT
+#define DSA_GATHER_SPLIT 128
+#endif
+#ifndef DSA_GATHER_UNROLL
+#define DSA_GATHER_UNROLL 4
+#endif
+constexpr int kGatherSplit = DSA_GATHER_SPLIT;    // kept tokens per split workgroup
+constexpr int kGatherUnroll = DSA_GATHER_UNROLL;  // tokens per lane slot with loads in flight together
 bool gather_supported(int H, int D);
 hipError_t launch_attn_gather(const GatherParams& p, int dtype, int D, hipStream_t st);
 

@@ -262,10 +262,11 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       for (int kk = 0; kk < KSTEPS; ++kk)
         bf[kk] = load_frag<T>(reinterpret_cast<const T*>(rowp + (32 * kk + 8 * g) * (int)sizeof(T)));
     };
+    // scores are streamed out with non-temporal stores (read once, by top-k)
     auto store = [&](int s, float e) {
       if (t_mine < a.T) {
-        if (s <= p_mine) srow[s] = e;
-        else if (a.write_upper) srow[s] = ninf;
+        if (s <= p_mine) __builtin_nontemporal_store(e, srow + s);
+        else if (a.write_upper) __builtin_nontemporal_store(ninf, srow + s);
       }
     };
     if (t_wave < a.T && s_tile + KT - 1 <= p_wave_last) {
@@ -344,8 +345,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
       const float e = score_subtile<T, DI, NQ>(f, bf);
       const int s = s_begin + sub * 16 + c;
       if (t_mine < a.T) {
-        if (s <= p_mine) srow[s] = e;
-        else if (a.write_upper) srow[s] = ninf;
+        if (s <= p_mine) __builtin_nontemporal_store(e, srow + s);
+        else if (a.write_upper) __builtin_nontemporal_store(ninf, srow + s);
       }
     };
     for (int sub = wave; sub < n_sub; sub += 8) {
