@@ -45,40 +45,35 @@ struct QueryFrags {
 
 // Loads the A fragments and head weights of queries t_first .. t_first+NQ-1.
 // Queries past T and heads past H_I read a valid row (finite data) and get
-// weight 0, so they add exact zeros; the loads carry no branches.
+// weight 0, so they add exact zeros. Every load is unconditional and issued
+// before any of them is used, so they all share one memory round trip.
 template <typename T, int DI, int NQ>
 __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const IndexerParams& a, int b,
                                              int t_first, int c, int g) {
   const T* qb = static_cast<const T*>(a.qidx) + (size_t)b * a.T * a.HI * DI;
   const float* wb = a.w + (size_t)b * a.T * a.HI;
+  float wr[NQ][2][4];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    const int t = t_first + j;
-    const bool tv = t < a.T;
-    const int tc = min(t, a.T - 1);
+    const int tc = min(t_first + j, a.T - 1);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int head = min(16 * rb + c, a.HI - 1);
 #pragma unroll
       for (int kk = 0; kk < QueryFrags<T, DI, NQ>::KSTEPS; ++kk)
         f.a[j][rb][kk] = load_frag<T>(qb + ((size_t)tc * a.HI + head) * DI + 32 * kk + 8 * g);
-      // weights of heads 16*rb + 4*g + (0..3): one 16-byte load when H_I is a
-      // multiple of 4 (the row stays 16-byte aligned), else four scalar loads
-      const int h4 = 16 * rb + 4 * g;
-      if ((a.HI & 3) == 0) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(wb + (size_t)tc * a.HI + min(h4, a.HI - 4));
-        const float keep = (tv && h4 < a.HI) ? 1.f : 0.f;
+      // weights of heads 16*rb + 4*g + (0..3)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) f.w[j][rb][r] = wv[r] * keep;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float wv = wb[(size_t)tc * a.HI + min(h4 + r, a.HI - 1)];
-          f.w[j][rb][r] = wv * ((tv && h4 + r < a.HI) ? 1.f : 0.f);
-        }
-      }
+      for (int r = 0; r < 4; ++r) wr[j][rb][r] = wb[(size_t)tc * a.HI + min(16 * rb + 4 * g + r, a.HI - 1)];
     }
   }
+#pragma unroll
+  for (int j = 0; j < NQ; ++j)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        f.w[j][rb][r] = (t_first + j < a.T && 16 * rb + 4 * g + r < a.HI) ? wr[j][rb][r] : 0.f;
 }
 
 // Scores of the wave's (up to 4) queries against one 16-key subtile whose B
@@ -184,13 +179,42 @@ struct UnitMap {
   }
 };
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_wave_base + 16 l (lds_wave_base is the same for the whole wave).
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+// B fragment (elements 32 kk + 8 g .. +7) of a key row stored with its
+// 16-byte chunks permuted by XOR with sw.
+template <typename T> __device__ __forceinline__ frag_t<T> lds_frag(const unsigned char* rowp, int kk, int g, int sw);
+template <> __device__ __forceinline__ bf16x8 lds_frag<bf16>(const unsigned char* rowp, int kk, int g, int sw) {
+  return *reinterpret_cast<const bf16x8*>(rowp + (((4 * kk + g) ^ sw) << 4));
+}
+template <> __device__ __forceinline__ f32x8 lds_frag<float>(const unsigned char* rowp, int kk, int g, int sw) {
+  const f32x4 lo = *reinterpret_cast<const f32x4*>(rowp + (((8 * kk + 2 * g) ^ sw) << 4));
+  const f32x4 hi = *reinterpret_cast<const f32x4*>(rowp + (((8 * kk + 2 * g + 1) ^ sw) << 4));
+  return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Key tiles go from HBM straight into LDS (global_load_lds, 16 bytes per
+// lane), double-buffered: one 64-key tile of the next unit is in flight while
+// the current one is scored. A tile's rows are stored unpadded, each row's
+// 16-byte chunks permuted (physical chunk = chunk ^ (row mod CH16)) so that
+// the 16 lanes reading one chunk column of 16 consecutive rows hit distinct
+// banks. The scores of a unit are stored one unit late, right after the next
+// tile's loads are issued, so the wait for a tile never waits on the stores
+// of the unit just scored.
 template <typename T, int DI>
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a, UnitMap um,
                                                                           long long n_units) {
-  constexpr int NT = 64 * kIdxWaves, KT = kIdxKT, KSTEPS = DI / 32;
-  constexpr int ROWB = DI * (int)sizeof(T), PITCH = ROWB + 16, CH16 = ROWB / 16;
-  constexpr int TOT16 = KT * CH16, N16 = (TOT16 + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * KT * PITCH];
+  constexpr int KT = kIdxKT, KSTEPS = DI / 32, NSUB = KT / 16;
+  constexpr int ROWB = DI * (int)sizeof(T), CH16 = ROWB / 16;
+  constexpr int TILEB = KT * ROWB, NINST = TILEB / 1024;  // 1 KiB (64 lanes x 16 B) per instruction
+  static_assert(TILEB % 1024 == 0 && (CH16 & (CH16 - 1)) == 0, "tile layout");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const long long u0 = (long long)blockIdx.x * n_units / gridDim.x;
@@ -199,39 +223,65 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   const float ninf = fneg_inf();
   const int jl = ((g & 1) << 1) | (g >> 1);  // query of the wave whose score this lane ends up with
 
-  // Key tiles of the range, staged through LDS (double-buffered): unit u's
-  // tile is loaded while unit u-1 is scored.
-  u32x4 stg[N16];
-  auto gload = [&](int b, int kt) {
-    const T* kb = static_cast<const T*>(a.kidx) + (size_t)b * a.kv_cap * DI;
+  // Loader: instruction j (waves take j = wave, wave + NW, ...) fills LDS
+  // bytes [1024 j, 1024 j + 1024); lane l writes physical chunk L % CH16 of
+  // row L / CH16 (L = 64 j + l) and so fetches the logical chunk the
+  // permutation puts there. Rows past n_kv read the last cached key: finite
+  // data whose scores are never stored.
+  constexpr int NJ = (NINST + kIdxWaves - 1) / kIdxWaves;
+  int dl_row[NJ], dl_chunk[NJ];
 #pragma unroll
-    for (int n = 0; n < N16; ++n) {
-      const int i = tid + n * NT;
-      if (i < TOT16) {
-        const int s = min(kt * KT + i / CH16, a.n_kv - 1);  // keys past n_kv: a valid row, never stored
-        stg[n] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kb + (size_t)s * DI) + (i % CH16) * 16);
+  for (int n = 0; n < NJ; ++n) {
+    const int L = (wave + n * kIdxWaves) * 64 + lane;
+    dl_row[n] = L / CH16;
+    dl_chunk[n] = (L % CH16) ^ (dl_row[n] & (CH16 - 1));
+  }
+  const char* kcache = static_cast<const char*>(a.kidx);
+  auto dload = [&](int b, int kt, int buf) {
+    const char* kb = kcache + (size_t)b * a.kv_cap * ROWB;
+#pragma unroll
+    for (int n = 0; n < NJ; ++n) {
+      const int j = wave + n * kIdxWaves;
+      if (NINST % kIdxWaves == 0 || j < NINST) {
+        const int s = min(kt * KT + dl_row[n], a.n_kv - 1);
+        dma16(kb + (size_t)s * ROWB + dl_chunk[n] * 16, lds + buf * TILEB + j * 1024);
       }
     }
   };
-  auto lstore = [&](int buf) {
+  // B operand of key subtile sub: row 16 sub + c, elements 32 kk + 8 g .. +7
+  auto load_b = [&](int buf, int sub, frag_t<T> (&bf)[KSTEPS]) {
+    const int row = sub * 16 + c;
+    const unsigned char* rowp = lds + buf * TILEB + row * ROWB;
 #pragma unroll
-    for (int n = 0; n < N16; ++n) {
-      const int i = tid + n * NT;
-      if (i < TOT16)
-        *reinterpret_cast<u32x4*>(lds + buf * KT * PITCH + (i / CH16) * PITCH + (i % CH16) * 16) = stg[n];
-    }
+    for (int kk = 0; kk < KSTEPS; ++kk) bf[kk] = lds_frag<T>(rowp, kk, g, row & (CH16 - 1));
   };
 
   int b, qt, kt;
   um.decode(u0, b, qt, kt);
-  gload(b, kt);
-  lstore(0);
-  __syncthreads();
+  dload(b, kt, 0);
 
   QueryFrags<T, DI, QPW> f;
   int cur_b = -1, cur_qt = -1;
-  int t_wave = 0, p_wave_last = -1, t_mine = 0, p_mine = 0;
-  float* srow = nullptr;
+  int t_wave = 0, p_wave_last = -1, p_mine = 0;
+  float* srow = nullptr;  // this lane's score row, or nullptr when its query is past T
+  // scores of the previous unit, stored one unit late
+  float pend[NSUB];
+  float* pend_row = nullptr;
+  int pend_s0 = 0, pend_p = 0;
+  auto flush = [&]() {
+    if (pend_row) {
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        const int s = pend_s0 + sub * 16 + c;
+        // scores are streamed out with non-temporal stores (read once, by top-k)
+        if (s <= pend_p) __builtin_nontemporal_store(pend[sub], pend_row + s);
+        else if (a.write_upper) __builtin_nontemporal_store(ninf, pend_row + s);
+      }
+    }
+  };
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
   for (long long u = u0; u < u1; ++u) {
     const int buf = (int)((u - u0) & 1);
     // next unit
@@ -243,7 +293,6 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
         ++nb;
       }
     }
-    if (u + 1 < u1) gload(nb, nkt);
     if (b != cur_b || qt != cur_qt) {
       cur_b = b;
       cur_qt = qt;
@@ -251,51 +300,39 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       const int nq = max(0, min(QPW, a.T - t_wave));
       p_wave_last = a.q_pos0 + t_wave + nq - 1;
       load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
-      t_mine = t_wave + jl;
+      const int t_mine = t_wave + jl;
       p_mine = a.q_pos0 + t_mine;
-      srow = a.scores + ((size_t)b * a.T + min(t_mine, a.T - 1)) * a.Lpad;
+      srow = t_mine < a.T ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
     }
+    if (u + 1 < u1) dload(nb, nkt, buf ^ 1);
+    flush();
+
     const int s_tile = kt * KT;
-    auto load_b = [&](int sub, frag_t<T> (&bf)[KSTEPS]) {
-      const unsigned char* rowp = lds + buf * KT * PITCH + (sub * 16 + c) * PITCH;
+    float cur[NSUB];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        bf[kk] = load_frag<T>(reinterpret_cast<const T*>(rowp + (32 * kk + 8 * g) * (int)sizeof(T)));
-    };
-    // scores are streamed out with non-temporal stores (read once, by top-k)
-    auto store = [&](int s, float e) {
-      if (t_mine < a.T) {
-        if (s <= p_mine) __builtin_nontemporal_store(e, srow + s);
-        else if (a.write_upper) __builtin_nontemporal_store(ninf, srow + s);
-      }
-    };
-    if (t_wave < a.T && s_tile + KT - 1 <= p_wave_last) {
-      // Whole tile below the wave's last query.
-#pragma unroll
-      for (int sub = 0; sub < KT / 16; ++sub) {
+    for (int sub = 0; sub < NSUB; ++sub) {
+      cur[sub] = ninf;
+      if (t_wave < a.T && s_tile + sub * 16 <= p_wave_last) {
         frag_t<T> bf[KSTEPS];
-        load_b(sub, bf);
-        store(s_tile + sub * 16 + c, score_subtile<T, DI, QPW>(f, bf));
-      }
-    } else if (t_wave < a.T) {
-#pragma unroll
-      for (int sub = 0; sub < KT / 16; ++sub) {
-        const int s_sub = s_tile + sub * 16;
-        if (s_sub <= p_wave_last) {
-          frag_t<T> bf[KSTEPS];
-          load_b(sub, bf);
-          store(s_sub + c, score_subtile<T, DI, QPW>(f, bf));
-        } else if (a.write_upper && t_mine < a.T) {
-          srow[s_sub + c] = ninf;
-        }
+        load_b(buf, sub, bf);
+        cur[sub] = score_subtile<T, DI, QPW>(f, bf);
       }
     }
-    if (u + 1 < u1) lstore(buf ^ 1);
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) pend[sub] = cur[sub];
+    pend_row = srow;
+    pend_s0 = s_tile;
+    pend_p = p_mine;
+
+    // the next tile has landed (every wave waits for its own loads) before
+    // any wave reads it
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     b = nb;
     qt = nqt;
     kt = nkt;
   }
+  flush();
 }
 
 // -inf for the columns past each query tile's last key tile (scores rows of
