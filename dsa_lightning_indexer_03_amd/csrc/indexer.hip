@@ -157,6 +157,15 @@ struct UnitMap {
     if (n > nfull) s += ntk(nfull);
     return s;
   }
+  // Query tiles are visited short and long alternately (position i holds
+  // tile i/2 for even i, nqt-1-i/2 for odd i), so that any run of units
+  // crosses few query tiles and the q-fragment reloads spread evenly over
+  // the workgroups' equal ranges.
+  __device__ __host__ int qt_at(int i) const { return (i & 1) ? nqt - 1 - (i >> 1) : (i >> 1); }
+  // units of positions 0..n-1: tiles 0..ceil(n/2)-1 and nqt-floor(n/2)..nqt-1
+  __device__ __host__ long long prefix_pos(int n) const {
+    return prefix((n + 1) >> 1) + per_seq - prefix(nqt - (n >> 1));
+  }
   __device__ __host__ void init(int T_, int q_pos0_) {
     T = T_;
     q_pos0 = q_pos0_;
@@ -164,18 +173,18 @@ struct UnitMap {
     nfull = T / kIdxQT;
     per_seq = prefix(nqt);
   }
-  // (b, qt, kt) of unit u
-  __device__ void decode(long long u, int& b, int& qt, int& kt) const {
+  // (b, position, kt) of unit u
+  __device__ void decode(long long u, int& b, int& pos, int& kt) const {
     b = (int)(u / per_seq);
     const long long v = u - (long long)b * per_seq;
-    int lo = 0, hi = nqt - 1;  // largest qt with prefix(qt) <= v
+    int lo = 0, hi = nqt - 1;  // largest position with prefix_pos(pos) <= v
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (prefix(mid) <= v) lo = mid;
+      if (prefix_pos(mid) <= v) lo = mid;
       else hi = mid - 1;
     }
-    qt = lo;
-    kt = (int)(v - prefix(lo));
+    pos = lo;
+    kt = (int)(v - prefix_pos(lo));
   }
 };
 
@@ -199,22 +208,38 @@ template <> __device__ __forceinline__ f32x8 lds_frag<float>(const unsigned char
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Key tiles go from HBM straight into LDS (global_load_lds, 16 bytes per
-// lane), double-buffered: one 64-key tile of the next unit is in flight while
-// the current one is scored. A tile's rows are stored unpadded, each row's
-// 16-byte chunks permuted (physical chunk = chunk ^ (row mod CH16)) so that
-// the 16 lanes reading one chunk column of 16 consecutive rows hit distinct
-// banks. The scores of a unit are stored one unit late, right after the next
-// tile's loads are issued, so the wait for a tile never waits on the stores
-// of the unit just scored.
+#ifndef DSA_IDX_STAGES
+#define DSA_IDX_STAGES 3
+#endif
+constexpr int kIdxStages = DSA_IDX_STAGES;  // key tiles in the LDS ring (kIdxStages - 1 in flight)
+static_assert(kIdxStages >= 2 && kIdxStages <= 6, "LDS ring depth");
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Key tiles go from HBM (L2 in practice: every tile is reused by all query
+// tiles) straight into LDS with global_load_lds, 16 bytes per lane, through
+// a ring of kIdxStages tiles: the tiles of the next kIdxStages-1 units are in
+// flight while the current one is scored. Every iteration issues the same
+// number of tile loads (past the end of the range the last tile is loaded
+// again), after the score stores, so "tile u+1 has landed" is a count: at
+// most (kIdxStages-2) x loads-per-tile operations may still be outstanding
+// (a wave that loads nothing for a tile has nothing to wait for). The
+// workgroup barrier carries no memory fence, so the scores stored earlier
+// are not waited for. A tile's rows are stored unpadded, each row's 16-byte
+// chunks permuted (physical chunk = chunk ^ (row mod CH16)) so that the 16
+// lanes reading one chunk column of 16 consecutive rows hit distinct banks.
+// The scores of a unit are stored one unit late, after the next tile loads
+// are issued.
 template <typename T, int DI>
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a, UnitMap um,
                                                                           long long n_units) {
-  constexpr int KT = kIdxKT, KSTEPS = DI / 32, NSUB = KT / 16;
+  constexpr int KT = kIdxKT, KSTEPS = DI / 32, NSUB = KT / 16, S = kIdxStages;
   constexpr int ROWB = DI * (int)sizeof(T), CH16 = ROWB / 16;
   constexpr int TILEB = KT * ROWB, NINST = TILEB / 1024;  // 1 KiB (64 lanes x 16 B) per instruction
   static_assert(TILEB % 1024 == 0 && (CH16 & (CH16 - 1)) == 0, "tile layout");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * TILEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[S * TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const long long u0 = (long long)blockIdx.x * n_units / gridDim.x;
@@ -224,41 +249,74 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   const int jl = ((g & 1) << 1) | (g >> 1);  // query of the wave whose score this lane ends up with
 
   // Loader: instruction j (waves take j = wave, wave + NW, ...) fills LDS
-  // bytes [1024 j, 1024 j + 1024); lane l writes physical chunk L % CH16 of
-  // row L / CH16 (L = 64 j + l) and so fetches the logical chunk the
-  // permutation puts there. Rows past n_kv read the last cached key: finite
-  // data whose scores are never stored.
+  // bytes [1024 j, 1024 j + 1024) of a ring slot; lane l writes physical
+  // chunk L % CH16 of row L / CH16 (L = 64 j + l) and so fetches the logical
+  // chunk the permutation puts there. Rows past n_kv read the last cached
+  // key: finite data whose scores are never stored.
   constexpr int NJ = (NINST + kIdxWaves - 1) / kIdxWaves;
-  int dl_row[NJ], dl_chunk[NJ];
+  constexpr bool kAllWavesLoad = NINST % kIdxWaves == 0;
+  static_assert(kAllWavesLoad || NINST < kIdxWaves, "tile loads split evenly or fit in one round");
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy, kept in a scalar register
+  uint32_t dl_off[NJ];  // byte offset of this lane's 16 bytes from the tile's first key row
+  int dl_row[NJ];
 #pragma unroll
   for (int n = 0; n < NJ; ++n) {
-    const int L = (wave + n * kIdxWaves) * 64 + lane;
+    const int L = (wave_u + n * kIdxWaves) * 64 + lane;
     dl_row[n] = L / CH16;
-    dl_chunk[n] = (L % CH16) ^ (dl_row[n] & (CH16 - 1));
+    dl_off[n] = (uint32_t)(dl_row[n] * ROWB + (((L % CH16) ^ (dl_row[n] & (CH16 - 1))) << 4));
   }
   const char* kcache = static_cast<const char*>(a.kidx);
-  auto dload = [&](int b, int kt, int buf) {
-    const char* kb = kcache + (size_t)b * a.kv_cap * ROWB;
+  auto dload = [&](int b, int kt, int slot) {
+    const int s0 = kt * KT;
+    const char* kb = kcache + ((size_t)b * a.kv_cap + s0) * ROWB;
+    unsigned char* dst = lds + slot * TILEB;
+    if (s0 + KT <= a.n_kv) {
 #pragma unroll
-    for (int n = 0; n < NJ; ++n) {
-      const int j = wave + n * kIdxWaves;
-      if (NINST % kIdxWaves == 0 || j < NINST) {
-        const int s = min(kt * KT + dl_row[n], a.n_kv - 1);
-        dma16(kb + (size_t)s * ROWB + dl_chunk[n] * 16, lds + buf * TILEB + j * 1024);
+      for (int n = 0; n < NJ; ++n) {
+        const int j = wave_u + n * kIdxWaves;
+        if (kAllWavesLoad || j < NINST) dma16(kb + dl_off[n], dst + j * 1024);
+      }
+    } else {  // last tile of the cache: rows past n_kv read the last cached key
+#pragma unroll
+      for (int n = 0; n < NJ; ++n) {
+        const int j = wave_u + n * kIdxWaves;
+        const int over = max(s0 + dl_row[n] - (a.n_kv - 1), 0);
+        if (kAllWavesLoad || j < NINST) dma16(kb + dl_off[n] - (size_t)over * ROWB, dst + j * 1024);
       }
     }
   };
   // B operand of key subtile sub: row 16 sub + c, elements 32 kk + 8 g .. +7
-  auto load_b = [&](int buf, int sub, frag_t<T> (&bf)[KSTEPS]) {
+  auto load_b = [&](int slot, int sub, frag_t<T> (&bf)[KSTEPS]) {
     const int row = sub * 16 + c;
-    const unsigned char* rowp = lds + buf * TILEB + row * ROWB;
+    const unsigned char* rowp = lds + slot * TILEB + row * ROWB;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) bf[kk] = lds_frag<T>(rowp, kk, g, row & (CH16 - 1));
   };
+  // unit cursor: (b, position, kt) -> the next unit; qt = um.qt_at(position)
+  auto advance = [&](int& b, int& pos, int& kt) {
+    if (++kt == um.ntk(um.qt_at(pos))) {
+      kt = 0;
+      if (++pos == um.nqt) {
+        pos = 0;
+        ++b;
+      }
+    }
+  };
 
-  int b, qt, kt;
-  um.decode(u0, b, qt, kt);
-  dload(b, kt, 0);
+  int b, qp, kt;
+  um.decode(u0, b, qp, kt);
+  // Prologue: tiles of units u0 .. u0+S-2 (clamped to the range's last unit).
+  int pb = b, ppos = qp, pkt = kt;  // prefetch cursor: the unit whose tile was loaded last
+  long long pu = u0;
+  dload(pb, pkt, 0);
+#pragma unroll
+  for (int i = 1; i < S - 1; ++i) {
+    if (pu + 1 < u1) {
+      advance(pb, ppos, pkt);
+      ++pu;
+    }
+    dload(pb, pkt, i);
+  }
 
   QueryFrags<T, DI, QPW> f;
   int cur_b = -1, cur_qt = -1;
@@ -279,20 +337,15 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       }
     }
   };
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // tile of u0 landed: the S-2 later tiles may still be in flight
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NJ));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 
+  int slot = 0;
   for (long long u = u0; u < u1; ++u) {
-    const int buf = (int)((u - u0) & 1);
-    // next unit
-    int nb = b, nqt = qt, nkt = kt + 1;
-    if (nkt == um.ntk(qt)) {
-      nkt = 0;
-      if (++nqt == um.nqt) {
-        nqt = 0;
-        ++nb;
-      }
-    }
+    const int qt = um.qt_at(qp);
     if (b != cur_b || qt != cur_qt) {
       cur_b = b;
       cur_qt = qt;
@@ -304,8 +357,15 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       p_mine = a.q_pos0 + t_mine;
       srow = t_mine < a.T ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
     }
-    if (u + 1 < u1) dload(nb, nkt, buf ^ 1);
+    // stores of unit u-1, then the tile of unit u+S-1 (or the range's last
+    // one again) into the slot read at unit u-1: the newest S-2 tile loads
+    // are then the last operations issued when tile u+1 is waited for
     flush();
+    if (pu + 1 < u1) {
+      advance(pb, ppos, pkt);
+      ++pu;
+    }
+    dload(pb, pkt, slot == 0 ? S - 1 : slot - 1);
 
     const int s_tile = kt * KT;
     float cur[NSUB];
@@ -314,7 +374,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       cur[sub] = ninf;
       if (t_wave < a.T && s_tile + sub * 16 <= p_wave_last) {
         frag_t<T> bf[KSTEPS];
-        load_b(buf, sub, bf);
+        load_b(slot, sub, bf);
         cur[sub] = score_subtile<T, DI, QPW>(f, bf);
       }
     }
@@ -324,15 +384,20 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     pend_s0 = s_tile;
     pend_p = p_mine;
 
-    // the next tile has landed (every wave waits for its own loads) before
-    // any wave reads it
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    b = nb;
-    qt = nqt;
-    kt = nkt;
+    // Tile u+1 has landed in every wave's part (each wave waits for its own
+    // loads; the S-2 tiles issued after it may still be in flight) before
+    // any wave reads it, and every wave is done with slot `slot` before it
+    // is refilled.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NJ));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    slot = slot == S - 1 ? 0 : slot + 1;
+    advance(b, qp, kt);
   }
   flush();
+  // no tile load may still be writing this workgroup's LDS when it exits
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // -inf for the columns past each query tile's last key tile (scores rows of
