@@ -134,7 +134,10 @@ __device__ __forceinline__ float score_subtile(const QueryFrags<T, DI, NQ>& f,
 #endif
 constexpr int kIdxWaves = DSA_IDX_WAVES;      // waves per workgroup, 4 queries each
 constexpr int kIdxQT = kIdxWaves * QPW;      // 32 queries per query tile
-constexpr int kIdxKT = 64;                    // keys per key tile
+#ifndef DSA_IDX_KT
+#define DSA_IDX_KT 64
+#endif
+constexpr int kIdxKT = DSA_IDX_KT;            // keys per key tile
 static_assert(kIdxKT % kIdxQT == 0, "query tile divides key tile");
 
 struct UnitMap {
@@ -242,8 +245,13 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   __shared__ __attribute__((aligned(1024))) unsigned char lds[S * TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
-  const long long u0 = (long long)blockIdx.x * n_units / gridDim.x;
-  const long long u1 = (long long)(blockIdx.x + 1) * n_units / gridDim.x;
+  // Workgroups are dealt to the 8 XCDs round-robin; the 1/8 of the unit
+  // sequence an XCD works on is contiguous, so neighbouring ranges (which
+  // share query tiles) share that XCD's L2.
+  const int G = gridDim.x;
+  const int r = (G % 8 == 0) ? (blockIdx.x % 8) * (G / 8) + blockIdx.x / 8 : blockIdx.x;
+  const long long u0 = (long long)r * n_units / G;
+  const long long u1 = (long long)(r + 1) * n_units / G;
   if (u0 >= u1) return;
   const float ninf = fneg_inf();
   const int jl = ((g & 1) << 1) | (g >> 1);  // query of the wave whose score this lane ends up with
