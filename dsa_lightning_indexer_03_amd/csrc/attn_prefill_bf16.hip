@@ -6,13 +6,15 @@
 // attention is the masked flash-attention path it feeds [aiaulis paras 2 and
 // 4; devotd section 2].
 //
-// Work split. A workgroup is 4 waves of one (sequence, head); each wave owns
+// Work split. A workgroup is 8 waves of one (sequence, head); each wave owns
 // 32 query rows (two blocks of 16, Q^T fragments in registers) and 64-key
 // tiles of K and V stream through LDS, double-buffered. Every K and V
 // fragment a wave reads from LDS is used for both of its query blocks (512 B
 // of LDS reads per key per wave against 32 * 512 flops of matrix work). At
-// at most 256 registers per lane two workgroups share a CU, two waves per
-// SIMD, so one wave's softmax overlaps the other's matrix work. (Waves of 64
+// at most 256 registers per lane one workgroup fills a CU, two waves per
+// SIMD, so one wave's softmax overlaps the other's matrix work; its 256
+// queries share each tile loaded into LDS (LDS bandwidth, shared by those
+// loads and the fragment reads, is what limits this kernel). (Waves of 64
 // queries halve the LDS traffic but need more than 256 registers: their
 // accumulators then live in AGPRs, which the compiler copies around every
 // tile, and they measured slower.)
@@ -59,7 +61,13 @@ constexpr float kLn2f = 0.69314718055994530942f;
 
 constexpr int kQB = 2;               // 16-query blocks per wave
 constexpr int kQW = 16 * kQB;        // queries per wave
-constexpr int kQT = 4 * kQW;        // queries per workgroup
+#ifndef DSA_ATTN_WAVES
+#define DSA_ATTN_WAVES 8
+#endif
+constexpr int kWaves = DSA_ATTN_WAVES;  // waves per workgroup
+constexpr int kQT = kWaves * kQW;     // queries per workgroup
+constexpr int kDL = kKT / (4 * kWaves);  // tile-load instructions per wave per K (or V) tile
+static_assert(kKT % (4 * kWaves) == 0, "each wave loads whole groups of four key rows");
 
 // Swizzle of a key row's 16-byte columns: physical column = col ^ swz(row).
 // swz is a bijection on row mod 16 (so the 16 rows a K fragment read touches
@@ -89,7 +97,7 @@ __device__ __forceinline__ float sum8_bf16(const bf16x8& p, float acc) {
   return acc;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStage];
 
@@ -141,16 +149,16 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
     l_run[qb] = 0.f;
   }
 
-  // Tile loader: wave w fills key rows 16w..16w+15 of the K and V tiles, four
-  // rows (1 KiB) per instruction; lane l writes physical column l % 16 of
+  // Tile loader: wave w fills key rows 4 kDL w .. 4 kDL (w+1) - 1 of the K and
+  // V tiles, four rows (1 KiB) per instruction; lane l writes physical column l % 16 of
   // row l / 16, so it fetches the logical column that the swizzle puts
   // there. Keys past n_kv (last tile only) read the last cached row instead:
   // finite data the mask gives zero weight.
-  int dl_row[4], dl_col[4];  // row of the tile and logical column this lane fetches, per instruction
-  uint32_t dl_off[4];        // element offset of that row/column from the tile's first key
+  int dl_row[kDL], dl_col[kDL];  // row of the tile and logical column this lane fetches, per instruction
+  uint32_t dl_off[kDL];          // element offset of that row/column from the tile's first key
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    dl_row[n] = 16 * wave + 4 * n + (lane >> 4);
+  for (int n = 0; n < kDL; ++n) {
+    dl_row[n] = 4 * kDL * wave + 4 * n + (lane >> 4);
     dl_col[n] = (lane & 15) ^ swz(dl_row[n]);
     dl_off[n] = (uint32_t)(dl_row[n] * kv_tok + dl_col[n] * 8);
   }
@@ -160,15 +168,15 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
     const size_t tbase = (size_t)s0 * kv_tok;
     if (s0 + kKT <= a.n_kv) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int r0 = 16 * wave + 4 * n;
+      for (int n = 0; n < kDL; ++n) {
+        const int r0 = 4 * kDL * wave + 4 * n;
         __builtin_amdgcn_global_load_lds(kbase + tbase + dl_off[n], (lds_void*)(st + r0 * kRow), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vbase + tbase + dl_off[n], (lds_void*)(st + kTileBytes + r0 * kRow), 16, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const int r0 = 16 * wave + 4 * n;
+      for (int n = 0; n < kDL; ++n) {
+        const int r0 = 4 * kDL * wave + 4 * n;
         const size_t off = (size_t)min(s0 + dl_row[n], a.n_kv - 1) * kv_tok + dl_col[n] * 8;
         __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)(st + r0 * kRow), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)(st + kTileBytes + r0 * kRow), 16, 0, 0);
@@ -363,7 +371,7 @@ hipError_t launch_attn_prefill_bf16(const AttnParams& p, hipStream_t st) {
   const int pairs_per_xcd = (pairs + 7) / 8;
   const long long nblocks = 8ll * n_qtiles * pairs_per_xcd;
   if (nblocks > 0x7fffffffll) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(attn_prefill_bf16_kernel, dim3((unsigned)nblocks), dim3(256), 0, st, p, n_qtiles,
+  hipLaunchKernelGGL(attn_prefill_bf16_kernel, dim3((unsigned)nblocks), dim3(64 * kWaves), 0, st, p, n_qtiles,
                      pairs_per_xcd);
   return hipGetLastError();
 }
