@@ -449,24 +449,44 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(GatherParams a) {
 }
 
 // One workgroup per (head, query row), one thread per output dim: the split
-// partials of that head are merged by their log-sum-exp. A row with no kept
-// token gets a zero output and lse = -inf.
+// partials of that head are merged by their log-sum-exp. Splits are taken 16
+// at a time with all their loads issued together (one memory round trip per
+// 16 splits instead of one per split). A row with no kept token gets a zero
+// output and lse = -inf.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_gather_combine_kernel(GatherParams a) {
+  constexpr int CH = 16;
   const int h = blockIdx.x, row = blockIdx.y, d = threadIdx.x;
   const int b = row / a.T, t = row % a.T, p = a.q_pos0 + t;
   const int count = a.counts ? a.counts[row] : min(a.top_k, p + 1);
   const int ns = max(1, (count + kGatherSplit - 1) / kGatherSplit);
   const float* ml = a.part_ml + (size_t)row * a.n_splits * a.H * 2 + 2 * h;
   const float* po = a.part_o + (size_t)row * a.n_splits * a.H * D + (size_t)h * D + d;
-  float M = fneg_inf();
-  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[(size_t)j * a.H * 2]);
-  const float Mr = M == fneg_inf() ? 0.f : M;
-  float L = 0.f, O = 0.f;
-  for (int j = 0; j < ns; ++j) {
-    const float f = __builtin_amdgcn_exp2f(ml[(size_t)j * a.H * 2] - Mr);
-    L += f * ml[(size_t)j * a.H * 2 + 1];
-    O += f * po[(size_t)j * a.H * D];
+  const size_t mls = (size_t)a.H * 2, pos = (size_t)a.H * D;  // strides between splits
+  float M = fneg_inf(), L = 0.f, O = 0.f;
+  for (int j0 = 0; j0 < ns; j0 += CH) {
+    float m[CH], l[CH], o[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int j = min(j0 + i, ns - 1);  // past the last split: a valid split, weighted 0 below
+      m[i] = ml[j * mls];
+      l[i] = ml[j * mls + 1];
+      o[i] = po[j * pos];
+    }
+    float mc = M;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) mc = j0 + i < ns ? fmaxf(mc, m[i]) : mc;
+    const float mr = mc == fneg_inf() ? 0.f : mc;
+    const float alpha = __builtin_amdgcn_exp2f(M - mr);
+    L *= alpha;
+    O *= alpha;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const float f = j0 + i < ns ? __builtin_amdgcn_exp2f(m[i] - mr) : 0.f;
+      L = fmaf(f, l[i], L);
+      O = fmaf(f, o[i], O);
+    }
+    M = mc;
   }
   static_cast<T*>(a.out)[(((size_t)b * a.T + t) * a.H + h) * D + d] = from_float<T>(L > 0.f ? O / L : 0.f);
   if (a.lse && d == 0) a.lse[((size_t)b * a.T + t) * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : fneg_inf();
