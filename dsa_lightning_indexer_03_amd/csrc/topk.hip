@@ -21,10 +21,17 @@ __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   const int nmax = p.q_pos0 + p.T;  // longest candidate row in the call
   dim3 grid(p.T, p.B);
+  // Rows are latency-bound chains of barriers and LDS histograms, so the
+  // smallest workgroup that holds a row (keys in registers) wins: more rows
+  // are then in flight per CU.
   if (nmax <= 2048)
     hipLaunchKernelGGL((topk_mask_kernel<4, 8, 0>), grid, dim3(256), 0, st, p);
+  else if (nmax <= 4096)
+    hipLaunchKernelGGL((topk_mask_kernel<4, 16, 0>), grid, dim3(256), 0, st, p);
   else if (nmax <= 8192)
-    hipLaunchKernelGGL((topk_mask_kernel<8, 16, 0>), grid, dim3(512), 0, st, p);
+    hipLaunchKernelGGL((topk_mask_kernel<4, 32, 0>), grid, dim3(256), 0, st, p);
+  else if (nmax <= 16384)
+    hipLaunchKernelGGL((topk_mask_kernel<8, 32, 0>), grid, dim3(512), 0, st, p);
   else if (nmax <= 32768)
     hipLaunchKernelGGL((topk_mask_kernel<16, 32, 0>), grid, dim3(1024), 0, st, p);
   else if (nmax <= kTopkMaxRow)

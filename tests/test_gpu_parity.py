@@ -227,7 +227,8 @@ def test_edge_cases(edge):
         assert np.all(np.isneginf(to_np(sc[b])[:, wl.n_kv :]))
 
 
-@pytest.mark.parametrize("n_kv,T,top_k", [(300, 300, 37), (5000, 40, 1000), (20000, 6, 2048),
+@pytest.mark.parametrize("n_kv,T,top_k", [(300, 300, 37), (3500, 50, 2047), (5000, 40, 1000), (12000, 5, 2048),
+                                          (20000, 6, 2048),
                                           (65536, 3, 2048), (65536, 2, 65000)])
 def test_topk_kernel_on_crafted_scores(n_kv, T, top_k):
     """The top-k op alone on float32 rows full of ties (integers in [-3, 3],
