@@ -43,21 +43,17 @@
 // Scheduling. Workgroup ids are mapped so that all query tiles of one
 // (sequence, head) pair land on the same XCD (id mod 8), sharing its L2 for
 // the K/V stream, and the query tiles with the most keys are dispatched first.
+#include "attn_bf16_common.hpp"
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
 namespace dsa {
 namespace {
 
-constexpr int kD = 128;             // head dim
-constexpr int kKT = 64;             // keys per tile
-constexpr int kKS = kD / 32;        // k-steps of S^T (head dim / 32)
-constexpr int kDB = kD / 16;        // 16-dim blocks of O^T
-constexpr int kRow = kD * 2;                 // bytes per key row in LDS (K and V)
-constexpr int kTileBytes = kKT * kRow;       // one 64-key tile of K or V
+using namespace attn_bf16;
+
 constexpr int kStage = 2 * kTileBytes;       // K tile then V tile
-constexpr float kLazyMax = 8.0f;             // log2 units
-constexpr float kLn2f = 0.69314718055994530942f;
+
 
 constexpr int kQB = 2;               // 16-query blocks per wave
 constexpr int kQW = 16 * kQB;        // queries per wave
@@ -69,32 +65,10 @@ constexpr int kQT = kWaves * kQW;     // queries per workgroup
 constexpr int kDL = kKT / (4 * kWaves);  // tile-load instructions per wave per K (or V) tile
 static_assert(kKT % (4 * kWaves) == 0, "each wave loads whole groups of four key rows");
 
-// Swizzle of a key row's 16-byte columns: physical column = col ^ swz(row).
-// swz is a bijection on row mod 16 (so the 16 rows a K fragment read touches
-// land in 16 different columns) and, within every aligned group of four
-// rows, differs in its upper three bits (so the four rows x two columns a
-// 16-lane transpose read touches land in eight different columns).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
-// Byte offset of 16-byte column `col` of key row `row` in a swizzled tile.
-__device__ __forceinline__ int tile_off(int row, int col) { return row * kRow + ((col ^ swz(row)) << 4); }
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) void lds_void;
-
 __device__ __forceinline__ float mask_elem(float s, uint32_t word, int bit) {
   // all-ones when bit `bit` of word is set, else zero; then keep s or -inf
   const int m = (int)(word << (31 - bit)) >> 31;
   return __int_as_float((m & __float_as_int(s)) | (~m & (int)0xff800000u));
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float sum8_bf16(const bf16x8& p, float acc) {
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p[2 * i], p[2 * i + 1]}, one, acc, false);
-  return acc;
 }
 
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -314,15 +288,7 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
           for (int db = 0; db < kDB; ++db) {
-            // keys 32*ks + 16*hf + 4*g + (0..3), dim 16*db + c, for hf = 0, 1
-            v4i16 t[2];
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              const int row = 32 * ks + 16 * hf + 4 * g + (c >> 2), j = c & 3;
-              t[hf] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (lds_v4i16*)(vl + tile_off(row, 2 * db + (j >> 1)) + 8 * (j & 1)));
-            }
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            const bf16x8 vf = vt_frag(vl, ks, db, c, g);
 #pragma unroll
             for (int qb = 0; qb < kQB; ++qb) o[db][qb] = mma_kstep(vf, pf[qb][ks], o[db][qb]);
           }

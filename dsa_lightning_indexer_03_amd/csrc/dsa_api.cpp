@@ -98,6 +98,13 @@ dsa_status check_ptr(const void* p, const char* name, bool required = true) {
 // The gather (decode) attention path runs for few queries per sequence.
 bool use_gather(const dsa_dims& d) { return d.n_q <= 8 && dsa::gather_supported(d.heads, d.head_dim); }
 
+// Prefill-shaped forward calls with one K/V row per token (kv_heads == 1)
+// attend over the top-k index list directly (gather + MFMA with the heads as
+// M) instead of the masked-dense tile loop.
+bool use_mqa_list(const dsa_dims& d) {
+  return !use_gather(d) && d.dtype == DSA_BF16 && dsa::attn_mqa_bf16_supported(d.heads, d.kv_heads, d.head_dim);
+}
+
 int gather_splits(int64_t max_kept) { return (int)((max_kept + dsa::kGatherSplit - 1) / dsa::kGatherSplit); }
 
 // Workspace layouts. Every region starts 256-B aligned.
@@ -107,11 +114,23 @@ struct AttnWs {
 };
 AttnWs attn_ws(const dsa_dims& d, bool have_list) {
   AttnWs w;
-  if (!use_gather(d)) return w;
+  const bool mqa = use_mqa_list(d);
+  if (!use_gather(d) && !mqa) return w;
   const int64_t rows = (int64_t)d.batch * d.n_q;
   const int64_t max_p1 = (int64_t)d.q_pos0 + d.n_q;
   int64_t max_kept = max_p1;
   size_t off = 0;
+  if (mqa) {  // a kept-token list per row (compacted from the mask when none is given)
+    if (!have_list) {
+      w.list_stride = (int)max_p1;
+      w.list = off;
+      off += align_up((size_t)rows * w.list_stride * 4);
+      w.counts = off;
+      off += align_up((size_t)rows * 4);
+    }
+    w.total = off;
+    return w;
+  }
   if (!have_list) {
     w.list_stride = (int)max_p1;
     w.list = off;
@@ -145,7 +164,7 @@ FwdWs fwd_ws(const dsa_dims& d, bool user_mask, bool user_indices) {
     w.mask = off;
     off += align_up((size_t)rows * (lp / 32) * 4);
   }
-  const bool gather = use_gather(d);
+  const bool gather = use_gather(d) || use_mqa_list(d);
   if (gather && !user_indices) {
     w.indices = off;
     off += align_up((size_t)rows * d.top_k * 4);
@@ -193,7 +212,8 @@ dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const 
                          const int32_t* list, void* out, float* lse, unsigned char* ws, const AttnWs& aw,
                          hipStream_t st) {
   const float scale_log2 = d.scale * 1.4426950408889634f;
-  if (!use_gather(d)) {
+  const bool mqa = use_mqa_list(d);
+  if (!use_gather(d) && !mqa) {
     dsa::AttnParams p{};
     p.q = q;
     p.k = k;
@@ -237,6 +257,19 @@ dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const 
     g.list_stride = aw.list_stride;
   }
   g.top_k = d.top_k;
+  if (mqa) {
+    g.out = out;
+    g.lse = lse;
+    g.B = d.batch;
+    g.T = d.n_q;
+    g.q_pos0 = d.q_pos0;
+    g.n_kv = d.n_kv;
+    g.kv_cap = d.kv_capacity;
+    g.H = d.heads;
+    g.Hkv = d.kv_heads;
+    g.scale_log2 = scale_log2;
+    return hip_status(dsa::launch_attn_mqa_bf16(g, st), "kept-list attention launch", st);
+  }
   g.part_o = reinterpret_cast<float*>(ws + aw.part_o);
   g.part_ml = reinterpret_cast<float*>(ws + aw.part_ml);
   g.out = out;
@@ -324,10 +357,12 @@ dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, c
   float* scores = reinterpret_cast<float*>(wsb + fw.scores);
   uint32_t* m = mask ? mask : reinterpret_cast<uint32_t*>(wsb + fw.mask);
   const bool gather = use_gather(d);
-  int32_t* idx = indices ? indices : (gather ? reinterpret_cast<int32_t*>(wsb + fw.indices) : nullptr);
+  const bool mqa = use_mqa_list(d);
+  int32_t* idx = indices ? indices : (gather || mqa ? reinterpret_cast<int32_t*>(wsb + fw.indices) : nullptr);
   DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
   DSA_TRY(run_topk(d, scores, m, idx, st));
-  DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw, st));
+  DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather || mqa ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw,
+                        st));
   return ok();
 }
 

@@ -69,6 +69,11 @@ constexpr int kGatherSplit = DSA_GATHER_SPLIT;    // kept tokens per split workg
 constexpr int kGatherUnroll = DSA_GATHER_UNROLL;  // tokens per lane slot with loads in flight together
 bool gather_supported(int H, int D);
 hipError_t launch_attn_gather(const GatherParams& p, int dtype, int D, hipStream_t st);
+// bf16, head dim 128, one K/V row per token (kv_heads == 1), prefill-shaped
+// calls: one wave per query over its kept-token list (attn_mqa_bf16.hip);
+// part_o / part_ml / n_splits are not used.
+bool attn_mqa_bf16_supported(int H, int Hkv, int D);
+hipError_t launch_attn_mqa_bf16(const GatherParams& p, hipStream_t st);
 
 // Compacts mask rows (bits s <= p, s < n_kv) into ascending token lists.
 struct CompactParams {

@@ -114,6 +114,14 @@ WORKLOADS = {
             description="long-context prefill, L=65536 in 16 chunks of 4096 "
                         "queries against the growing cache",
         ),
+        Workload(
+            name="longctx_mqa_bf16_L65536_chunk4096",
+            dtype="bf16", batch=1, n_q=65536, q_pos0=0, n_kv=65536,
+            idx_heads=32, idx_dim=128, top_k=2048, heads=32, kv_heads=1, head_dim=128,
+            seed=6, chunks=16, qidx_std=_ws(128), kidx_std=_ws(128), w_std=_ws(32),
+            description="long-context prefill as above with one K/V row per token "
+                        "shared by all 32 heads (the key-only cache reading)",
+        ),
     ]
 }
 

@@ -194,6 +194,10 @@ EDGE = [
     ("integer_ties_ragged", "bf16", 1, 300, 0, 300, 300, 32, 128, 40, 8, 8, 128, True),
     ("decode_integer_ties", "bf16", 4, 1, 2999, 3000, 3000, 32, 128, 333, 32, 32, 128, True),
     ("long_rows_topk_lds", "bf16", 1, 9, 40000, 40009, 40009, 32, 128, 2048, 8, 8, 64, False),
+    # one K/V row per token: prefill attends over the top-k index list
+    ("mqa_prefill_ragged", "bf16", 2, 130, 37, 167, 170, 32, 128, 50, 32, 1, 128, False),
+    ("mqa_prefill_multi_tile", "bf16", 1, 200, 500, 700, 700, 32, 128, 300, 32, 1, 128, False),
+    ("mqa_prefill_h16_ties", "bf16", 1, 300, 0, 300, 300, 32, 128, 40, 16, 1, 128, True),
 ]
 
 
@@ -255,7 +259,8 @@ def test_topk_kernel_on_crafted_scores(n_kv, T, top_k):
 @pytest.mark.parametrize("T,q_pos0,n_kv,H,Hkv,D,dt", [(130, 20, 200, 4, 2, 128, "bf16"),
                                                       (1, 700, 701, 8, 8, 64, "bf16"),
                                                       (6, 300, 306, 16, 4, 128, "bf16"),
-                                                      (3, 90, 93, 4, 4, 64, "fp32")])
+                                                      (3, 90, 93, 4, 4, 64, "fp32"),
+                                                      (100, 50, 150, 32, 1, 128, "bf16")])
 def test_sparse_attention_arbitrary_masks(T, q_pos0, n_kv, H, Hkv, D, dt):
     """The attention op alone on random masks (10% density, some empty rows,
     bits past the query position that must be ignored)."""
