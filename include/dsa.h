@@ -127,9 +127,13 @@ dsa_status dsa_topk_mask(const dsa_dims* dims, const float* scores, uint32_t* ma
  * empty S_i gives out = 0 and lse = -inf. lse (optional, may be NULL) is the
  * natural-log sum-exp of the scaled scores over S_i.
  * Prefill-shaped calls run a masked flash attention over 64-key tiles; calls
- * with few queries per sequence gather the kept rows instead. Both compute
- * the same function. Needs dsa_workspace_size(dims, DSA_OP_SPARSE_ATTENTION)
- * bytes of workspace. */
+ * with few queries per sequence gather the kept rows instead, and so do
+ * prefill-shaped bf16 calls with kv_heads == 1, head_dim 128 and 16 or 32
+ * heads (one K/V row per token serves every head; a key-only cache passes
+ * the same buffer as k_cache and v_cache). All compute the same function.
+ * Needs dsa_workspace_size(dims, DSA_OP_SPARSE_ATTENTION) bytes of
+ * workspace (for the kv_heads == 1 prefill case: an int32 kept-token list of
+ * q_pos0 + n_q entries per query row, compacted from the mask). */
 dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void* k_cache,
                                 const void* v_cache, const uint32_t* mask, void* out,
                                 float* lse, void* ws, size_t ws_bytes, void* stream);
@@ -137,7 +141,8 @@ dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void*
 /* The whole layer: dsa_index_scores -> dsa_topk_mask -> dsa_sparse_attention
  * with the scores kept in the workspace [aiaulis paras 2-4; devotd sections
  * 1-2]. `indices`, `mask` and `lse` are optional outputs (NULL = not
- * written; the mask then lives in the workspace). Needs
+ * written; the mask then lives in the workspace). Attention paths that
+ * gather kept rows read top-k's index list directly. Needs
  * dsa_workspace_size(dims, DSA_OP_FORWARD) bytes of workspace. */
 dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w,
                        const void* kidx, const void* q, const void* k_cache,
