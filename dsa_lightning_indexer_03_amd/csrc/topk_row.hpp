@@ -180,15 +180,19 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
 
   // Mask words: the ballot over element e is the word pair of tokens
   // [base + 64e, base + 64e + 64).
+  // Lane e keeps the ballot of element e (one mask word pair), so the pairs
+  // are stored by all lanes at once and the index list is built per word.
+  static_assert(EPT <= 64, "one mask word pair per lane");
   uint32_t running_eq = eq_base, nsel = 0;
+  uint64_t my_pair = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const uint64_t bs = ballot64(select(e, running_eq));
     nsel += (uint32_t)__popcll(bs);
-    const int wp = wave * EPT + e;
-    if (lane == 0 && 2 * wp < nwords)
-      *reinterpret_cast<uint2*>(mrow + 2 * wp) = make_uint2((uint32_t)bs, (uint32_t)(bs >> 32));
+    if (lane == e) my_pair = bs;
   }
+  if (lane < EPT && 2 * (wave * EPT + lane) < nwords)
+    *reinterpret_cast<uint2*>(mrow + 2 * (wave * EPT + lane)) = make_uint2((uint32_t)my_pair, (uint32_t)(my_pair >> 32));
   for (int wp = NW * EPT + tid; 2 * wp < nwords; wp += NT)
     *reinterpret_cast<uint2*>(mrow + 2 * wp) = make_uint2(0u, 0u);
 
@@ -197,14 +201,30 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
     __syncthreads();
     uint32_t off = 0;
     for (int w = 0; w < wave; ++w) off += red[w];
-    running_eq = eq_base;
+    if (4 * a.top_k < n) {
+      // Sparse rows: word pair e = lane covers tokens base + 64 lane + (0..63);
+      // each lane writes the few kept tokens of its own word.
+      const uint32_t cnt = (uint32_t)__popcll(my_pair);
+      uint32_t pos = off + wave_inclusive_sum(cnt) - cnt;
+      uint64_t bits = my_pair;
+      while (bits) {
+        const int bit = __ffsll((unsigned long long)bits) - 1;
+        if (pos < (uint32_t)a.top_k) irow[pos] = base + lane * 64 + bit;
+        ++pos;
+        bits &= bits - 1ull;
+      }
+    } else {
+      // Dense rows: element by element, consecutive lanes writing consecutive
+      // positions.
+      running_eq = eq_base;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const bool s = select(e, running_eq);
-      const uint64_t bs = ballot64(s);
-      const uint32_t pos = off + (uint32_t)__popcll(bs & lt);
-      if (s && pos < (uint32_t)a.top_k) irow[pos] = base + e * 64 + lane;
-      off += (uint32_t)__popcll(bs);
+      for (int e = 0; e < EPT; ++e) {
+        const bool sel = select(e, running_eq);
+        const uint64_t bs = ballot64(sel);
+        const uint32_t pos = off + (uint32_t)__popcll(bs & lt);
+        if (sel && pos < (uint32_t)a.top_k) irow[pos] = base + e * 64 + lane;
+        off += (uint32_t)__popcll(bs);
+      }
     }
   }
 }
