@@ -8,7 +8,8 @@ step of the layer runs in the library's kernels. There is no fallback: if the
 library is missing or a tensor is not on the GPU, calls raise.
 
 Entry points (same names as the C ABI, without the prefix):
-  index_scores, topk_mask, sparse_attention, forward, workspace_size
+  index_scores, topk_mask, sparse_attention, forward, forward_varlen,
+  workspace_size
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import torch  # imported before libdsa.so so both resolve to one HIP runtime
 __all__ = [
     "DsaError", "DSA_OP_INDEX_SCORES", "DSA_OP_TOPK_MASK", "DSA_OP_SPARSE_ATTENTION",
     "DSA_OP_FORWARD", "library_path", "lib", "make_dims", "index_scores", "topk_mask",
-    "sparse_attention", "forward", "workspace_size", "lpad",
+    "sparse_attention", "forward", "forward_varlen", "workspace_size", "lpad",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -55,6 +56,8 @@ _SIGS = {
                                             ctypes.c_size_t, _P]),
     "dsa_forward": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, ctypes.c_size_t, _P]),
+    "dsa_forward_varlen": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                          _P, _P, _P, ctypes.c_size_t, _P]),
     "dsa_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
     "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "dsa_last_error": (ctypes.c_char_p, []),
@@ -212,17 +215,23 @@ def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=Fals
 
 def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
             return_indices=True, return_mask=False, return_lse=False, workspace=None, out=None,
-            indices=None, mask=None, lse=None):
+            indices=None, mask=None, lse=None, seq_lens=None):
     """The whole DSA layer. Returns a dict with 'out' and the requested extras
     ('indices' [B, T, top_k] int32, 'mask' [B, T, Lpad/32] int32, 'lse').
     Passing `out`, `indices`, `mask`, `lse` or `workspace` tensors makes the
     call write into them instead of allocating (each passed extra is also
-    returned)."""
-    _need_gpu(qidx, w, kidx, q, k, v, workspace, out, indices, mask, lse)
+    returned). With `seq_lens` (int32 [B] on the GPU) the call goes to
+    dsa_forward_varlen: sequence b has seq_lens[b] cached tokens and its
+    queries are its last T positions; `n_kv` (default: the caches' capacity)
+    is the longest sequence and `q_pos0` is ignored."""
+    _need_gpu(qidx, w, kidx, q, k, v, workspace, out, indices, mask, lse, seq_lens)
     B, T, HI, DI = qidx.shape
     H, D = q.shape[2], q.shape[3]
     cap, Hkv = k.shape[1], k.shape[2]
     n_kv = cap if n_kv is None else n_kv
+    if seq_lens is not None:
+        _expect("seq_lens", seq_lens, (B,), torch.int32)
+        q_pos0 = n_kv - T
     _expect("w", w, (B, T, HI), torch.float32)
     _expect("kidx", kidx, (B, cap, DI), qidx.dtype)
     _expect("q", q, (B, T, H, D), qidx.dtype)
@@ -245,8 +254,16 @@ def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
         elif wanted:
             res[name] = torch.empty(shape, dtype=dt, device=dev)
     ws, nbytes = _workspace(d, DSA_OP_FORWARD, dev, workspace)
-    _check(lib().dsa_forward(ctypes.byref(d), _ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k),
-                             _ptr(v), _ptr(res["out"]), _ptr(res.get("lse")),
-                             _ptr(res.get("indices")), _ptr(res.get("mask")), _ptr(ws), nbytes,
-                             _stream(q)))
+    tail = (_ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k), _ptr(v), _ptr(res["out"]),
+            _ptr(res.get("lse")), _ptr(res.get("indices")), _ptr(res.get("mask")), _ptr(ws), nbytes,
+            _stream(q))
+    if seq_lens is None:
+        _check(lib().dsa_forward(ctypes.byref(d), *tail))
+    else:
+        _check(lib().dsa_forward_varlen(ctypes.byref(d), _ptr(seq_lens), *tail))
     return res
+
+
+def forward_varlen(qidx, w, kidx, q, k, v, seq_lens, *, top_k, **kw):
+    """forward() for a decode batch of different sequence lengths (see there)."""
+    return forward(qidx, w, kidx, q, k, v, top_k=top_k, seq_lens=seq_lens, **kw)

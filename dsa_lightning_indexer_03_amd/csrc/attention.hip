@@ -326,7 +326,10 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(GatherParams a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.y, split = blockIdx.x;
-  const int b = row / a.T, t = row % a.T, p = a.q_pos0 + t;
+  const int b = row / a.T, t = row % a.T;
+  int q_pos0, n_kv;
+  seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
+  const int p = q_pos0 + t;
   const int count = a.counts ? a.counts[row] : min(a.top_k, p + 1);
   const int ns = max(1, (count + SPLIT - 1) / SPLIT);  // an empty row still gets one split
   if (split >= ns) return;
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(GatherParams a) {
   // Kept-token lists come from the library's own top-k or mask compaction and
   // hold tokens in [0, n_kv); the clamp only guarantees that a corrupted list
   // can never address memory outside the caches.
-  for (int i = tid; i < ntok; i += 256) tok[i] = min(max(a.list[(size_t)row * a.list_stride + start + i], 0), a.n_kv - 1);
+  for (int i = tid; i < ntok; i += 256) tok[i] = min(max(a.list[(size_t)row * a.list_stride + start + i], 0), n_kv - 1);
   __syncthreads();
 
   const int group = a.H / a.Hkv;
@@ -457,7 +460,10 @@ template <typename T, int D>
 __global__ __launch_bounds__(D) void attn_gather_combine_kernel(GatherParams a) {
   constexpr int CH = 16;
   const int h = blockIdx.x, row = blockIdx.y, d = threadIdx.x;
-  const int b = row / a.T, t = row % a.T, p = a.q_pos0 + t;
+  const int b = row / a.T, t = row % a.T;
+  int q_pos0, n_kv;
+  seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
+  const int p = q_pos0 + t;
   const int count = a.counts ? a.counts[row] : min(a.top_k, p + 1);
   const int ns = max(1, (count + kGatherSplit - 1) / kGatherSplit);
   const float* ml = a.part_ml + (size_t)row * a.n_splits * a.H * 2 + 2 * h;

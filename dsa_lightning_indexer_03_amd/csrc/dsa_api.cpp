@@ -177,7 +177,7 @@ FwdWs fwd_ws(const dsa_dims& d, bool user_mask, bool user_indices) {
 }
 
 dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const void* kidx, float* scores,
-                      bool write_upper, hipStream_t st) {
+                      bool write_upper, hipStream_t st, const int32_t* seq_len = nullptr) {
   dsa::IndexerParams p{};
   p.qidx = qidx;
   p.w = w;
@@ -191,10 +191,12 @@ dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const
   p.HI = d.idx_heads;
   p.Lpad = (int)lpad_of(d);
   p.write_upper = write_upper ? 1 : 0;
+  p.seq_len = seq_len;
   return hip_status(dsa::launch_indexer(p, d.dtype, d.idx_dim, st), "indexer launch", st);
 }
 
-dsa_status run_topk(const dsa_dims& d, const float* scores, uint32_t* mask, int32_t* indices, hipStream_t st) {
+dsa_status run_topk(const dsa_dims& d, const float* scores, uint32_t* mask, int32_t* indices, hipStream_t st,
+                    const int32_t* seq_len = nullptr) {
   dsa::TopkParams p{};
   p.scores = scores;
   p.mask = mask;
@@ -205,12 +207,13 @@ dsa_status run_topk(const dsa_dims& d, const float* scores, uint32_t* mask, int3
   p.n_kv = d.n_kv;
   p.Lpad = (int)lpad_of(d);
   p.top_k = d.top_k;
+  p.seq_len = seq_len;
   return hip_status(dsa::launch_topk(p, st), "top-k launch", st);
 }
 
 dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const void* v, const uint32_t* mask,
                          const int32_t* list, void* out, float* lse, unsigned char* ws, const AttnWs& aw,
-                         hipStream_t st) {
+                         hipStream_t st, const int32_t* seq_len = nullptr) {
   const float scale_log2 = d.scale * 1.4426950408889634f;
   const bool mqa = use_mqa_list(d);
   if (!use_gather(d) && !mqa) {
@@ -283,6 +286,7 @@ dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const 
   g.Hkv = d.kv_heads;
   g.n_splits = aw.n_splits;
   g.scale_log2 = scale_log2;
+  g.seq_len = seq_len;
   return hip_status(dsa::launch_attn_gather(g, d.dtype, d.head_dim, st), "gather attention launch", st);
 }
 
@@ -363,6 +367,43 @@ dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, c
   DSA_TRY(run_topk(d, scores, m, idx, st));
   DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather || mqa ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw,
                         st));
+  return ok();
+}
+
+dsa_status dsa_forward_varlen(const dsa_dims* dims, const int32_t* seq_lens, const void* qidx, const float* w,
+                              const void* kidx, const void* q, const void* k_cache, const void* v_cache, void* out,
+                              float* lse, int32_t* indices, uint32_t* mask, void* ws, size_t ws_bytes,
+                              void* stream) {
+  DSA_TRY(check_dims(dims, true, true, true));
+  const dsa_dims& d = *dims;
+  if (d.q_pos0 != d.n_kv - d.n_q)
+    return fail(DSA_ERR_SHAPE, "varlen calls need q_pos0 == n_kv - n_q (got q_pos0 %d, n_kv %d, n_q %d)", d.q_pos0,
+                d.n_kv, d.n_q);
+  if (!use_gather(d))
+    return fail(DSA_ERR_UNSUPPORTED, "varlen calls support n_q <= 8 with the gather attention (n_q %d, heads %d, head_dim %d)",
+                d.n_q, d.heads, d.head_dim);
+  DSA_TRY(check_ptr(seq_lens, "seq_lens"));
+  DSA_TRY(check_ptr(qidx, "qidx"));
+  DSA_TRY(check_ptr(w, "w"));
+  DSA_TRY(check_ptr(kidx, "kidx"));
+  DSA_TRY(check_ptr(q, "q"));
+  DSA_TRY(check_ptr(k_cache, "k_cache"));
+  DSA_TRY(check_ptr(v_cache, "v_cache"));
+  DSA_TRY(check_ptr(out, "out"));
+  DSA_TRY(check_ptr(lse, "lse", false));
+  DSA_TRY(check_ptr(indices, "indices", false));
+  DSA_TRY(check_ptr(mask, "mask", false));
+  const FwdWs fw = fwd_ws(d, mask != nullptr, indices != nullptr);
+  DSA_TRY(check_ptr(ws, "workspace"));
+  if (ws_bytes < fw.total) return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, fw.total);
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* wsb = (unsigned char*)ws;
+  float* scores = reinterpret_cast<float*>(wsb + fw.scores);
+  uint32_t* m = mask ? mask : reinterpret_cast<uint32_t*>(wsb + fw.mask);
+  int32_t* idx = indices ? indices : reinterpret_cast<int32_t*>(wsb + fw.indices);
+  DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st, seq_lens));
+  DSA_TRY(run_topk(d, scores, m, idx, st, seq_lens));
+  DSA_TRY(run_attention(d, q, k_cache, v_cache, m, idx, out, lse, wsb + fw.attn, fw.aw, st, seq_lens));
   return ok();
 }
 

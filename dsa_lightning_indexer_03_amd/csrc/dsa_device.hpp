@@ -110,6 +110,20 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
 
 __device__ __forceinline__ float fneg_inf() { return __uint_as_float(0xff800000u); }
 
+// Cache extent of sequence b: the call's (q_pos0, n_kv), or, for a batch of
+// different lengths, its own length len (clamped to [T, n_kv]) with its T
+// queries at positions len - T .. len - 1.
+__device__ __forceinline__ void seq_extent(const int32_t* seq_len, int b, int T, int q_pos0, int n_kv, int& q0,
+                                           int& nkv) {
+  if (seq_len) {
+    nkv = min(max(seq_len[b], T), n_kv);
+    q0 = nkv - T;
+  } else {
+    nkv = n_kv;
+    q0 = q_pos0;
+  }
+}
+
 // bf16 <-> f32 on raw 16-bit patterns.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -15,6 +15,7 @@ struct IndexerParams {
   int B, T, q_pos0, n_kv, kv_cap, HI, Lpad;
   int key_chunk;      // keys per workgroup (multiple of 64)
   int write_upper;    // 1: write -inf for s > p; 0: leave those entries untouched
+  const int32_t* seq_len;  // [B] per-sequence cache lengths (decode kernel only), or nullptr
 };
 hipError_t launch_indexer(const IndexerParams& p, int dtype, int DI, hipStream_t st);
 
@@ -24,6 +25,7 @@ struct TopkParams {
   uint32_t* mask;       // [B][T][Lpad/32]
   int32_t* indices;     // [B][T][top_k] or nullptr
   int B, T, q_pos0, n_kv, Lpad, top_k;
+  const int32_t* seq_len;  // [B] per-sequence cache lengths, or nullptr
 };
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 
@@ -58,6 +60,7 @@ struct GatherParams {
   float* lse;             // [B][T][H] or nullptr
   int B, T, q_pos0, n_kv, kv_cap, H, Hkv, n_splits;
   float scale_log2;
+  const int32_t* seq_len;  // [B] per-sequence cache lengths (gather kernels), or nullptr
 };
 #ifndef DSA_GATHER_SPLIT
 #define DSA_GATHER_SPLIT 128

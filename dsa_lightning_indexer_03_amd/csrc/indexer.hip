@@ -428,15 +428,17 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
   constexpr int NT = 256, KSTEPS = DI / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int b = blockIdx.z, t_first = blockIdx.y * NQ, s_begin = blockIdx.x * a.key_chunk;
+  int q_pos0, n_kv;
+  seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
   const int nq = min(NQ, a.T - t_first);
-  const int p_last = a.q_pos0 + t_first + nq - 1;
+  const int p_last = q_pos0 + t_first + nq - 1;
   const int s_chunk_end = min(s_begin + a.key_chunk, a.Lpad);
   const int s_stop = min(s_chunk_end, p_last + 1);
   float* scores_b = a.scores + (size_t)b * a.T * a.Lpad;
   const float ninf = fneg_inf();
   const int jl = ((g & 1) << 1) | (g >> 1);
   const int t_mine = jl < nq ? t_first + jl : a.T;  // a.T: this lane stores nothing
-  const int p_mine = a.q_pos0 + t_mine;
+  const int p_mine = q_pos0 + t_mine;
   float* srow = scores_b + (size_t)t_mine * a.Lpad;
 
   if (s_begin < s_stop) {
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
     const int n_sub = (s_stop - s_begin + 15) / 16;
     auto load_b = [&](int sub, frag_t<T> (&bf)[KSTEPS]) {
       const int s = s_begin + sub * 16 + c;
-      const bool sv = s < a.n_kv;
+      const bool sv = s < n_kv;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
         bf[kk] = sv ? load_frag<T>(kb + (size_t)s * DI + 32 * kk + 8 * g) : zero_frag<T>();

@@ -57,7 +57,9 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
   uint32_t* found = sh.found;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int p = a.q_pos0 + t, n = p + 1;
+  int q_pos0, n_kv;
+  seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
+  const int p = q_pos0 + t, n = p + 1;
   const size_t row = (size_t)b * a.T + t;
   const int nwords = a.Lpad / 32;
   const float* srow = a.scores + row * a.Lpad;

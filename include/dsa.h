@@ -149,6 +149,30 @@ dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w,
                        const void* v_cache, void* out, float* lse, int32_t* indices,
                        uint32_t* mask, void* ws, size_t ws_bytes, void* stream);
 
+/* The whole layer, as dsa_forward, for a decode batch whose sequences have
+ * different lengths [aiaulis paras 2-4; devotd sections 1-2]. The pages
+ * describe one causal sequence; a batch is read as B independent layers that
+ * share one launch, so the result for sequence b is exactly dsa_forward's on
+ * that sequence alone. Sequence b holds
+ * len_b = clamp(seq_lens[b], n_q, n_kv) cached tokens, and its n_q queries sit
+ * at positions len_b - n_q .. len_b - 1: every candidate, score, kept index
+ * and attended key of sequence b lies below len_b; mask bits and scores past
+ * it are as for a row whose query sits at len_b - 1 (zero bits, never read).
+ *  - seq_lens: DEVICE int32 [batch], read by the kernels (values outside
+ *    [n_q, n_kv] are clamped to it; they are not checked on the host).
+ *  - dims->n_kv is the longest sequence (the row length of scores and mask,
+ *    Lpad = roundup(n_kv, 64)), and dims->q_pos0 must equal n_kv - n_q
+ *    (DSA_ERR_SHAPE otherwise), so that dsa_workspace_size(dims,
+ *    DSA_OP_FORWARD) sizes the workspace.
+ *  - Decode-shaped calls only: n_q <= 8 and a head configuration the
+ *    gather attention supports (DSA_ERR_UNSUPPORTED otherwise).
+ * Every other argument, layout and error behaviour is dsa_forward's. */
+dsa_status dsa_forward_varlen(const dsa_dims* dims, const int32_t* seq_lens, const void* qidx,
+                              const float* w, const void* kidx, const void* q,
+                              const void* k_cache, const void* v_cache, void* out, float* lse,
+                              int32_t* indices, uint32_t* mask, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* Workspace bytes `op` needs for `dims` (0 when none). Returns 0 for invalid
  * dims as well; the op itself then reports the error. Host only. */
 size_t dsa_workspace_size(const dsa_dims* dims, int32_t op);

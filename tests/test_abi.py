@@ -133,3 +133,24 @@ def test_binding_refuses_host_tensors():
     k = torch.zeros(1, 64, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         dsa.index_scores(q, w, k)
+
+
+def _varlen(d, seq=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return dsa.lib().dsa_forward_varlen(ctypes.byref(d), seq, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                        None, None, ws, ws_bytes, None)
+
+
+def test_forward_varlen_validation():
+    # decode-shaped: q_pos0 must be n_kv - n_q (the longest sequence's layout)
+    d = _dims(batch=4, n_q=1, q_pos0=10, n_kv=1000, kv_capacity=1000, top_k=300)
+    assert _varlen(d) == ERR_SHAPE
+    assert "q_pos0" in _err()
+    # prefill-shaped calls have no varlen kernel
+    d = _dims(batch=2, n_q=16, q_pos0=48, n_kv=64, kv_capacity=64)
+    assert _varlen(d) == ERR_UNSUPPORTED
+    d = _dims(batch=4, n_q=2, q_pos0=998, n_kv=1000, kv_capacity=1000, top_k=300)
+    assert _varlen(d, seq=None) == ERR_NULL
+    assert _varlen(d, seq=FAKE + 4) == ERR_MISALIGNED
+    need = dsa.workspace_size(d, dsa.DSA_OP_FORWARD)
+    assert need > 0
+    assert _varlen(d, ws_bytes=need - 1) == ERR_WORKSPACE

@@ -326,3 +326,72 @@ def test_chunked_prefill_equals_one_shot():
     torch.cuda.synchronize()
     assert torch.equal(torch.cat(idxs, 1), one["indices"])
     assert torch.equal(torch.cat(outs, 1), one["out"])
+
+
+# ------------------------------------------------------------------ decode batches of different lengths
+
+VARLEN = [
+    # name, dtype, T, cap, lens, HI, DI, k, H, Hkv, D, integer
+    ("varlen_mha_k2048", "bf16", 1, 5000, [5000, 1, 2048, 2049, 37, 4321], 32, 128, 2048, 32, 32, 128, False),
+    ("varlen_gqa_multi_query", "bf16", 3, 3000, [3, 2999, 1500, 700], 32, 128, 333, 16, 4, 64, False),
+    ("varlen_integer_ties", "bf16", 1, 3000, [3000, 2500, 64, 65], 32, 128, 40, 32, 32, 128, True),
+    ("varlen_fp32", "fp32", 2, 900, [900, 2, 400], 4, 32, 64, 4, 4, 64, False),
+]
+
+
+def _varlen_case(e):
+    name, dt, T, cap, lens, HI, DI, k, H, Hkv, D, integer = e
+    full = Workload(name=name, dtype=dt, batch=len(lens), n_q=cap, q_pos0=0, n_kv=cap, idx_heads=HI,
+                    idx_dim=DI, top_k=k, heads=H, kv_heads=Hkv, head_dim=D,
+                    seed=zlib.crc32(name.encode()) % 1000, integer_indexer=integer,
+                    qidx_std=1 / math.sqrt(DI), kidx_std=1.0, w_std=1 / math.sqrt(HI))
+    inp = make_inputs(full, "cpu")
+    # sequence b's queries are its positions len_b - T .. len_b - 1; the
+    # caches past len_b keep random data, which must never be read
+    for key in ("qidx", "w", "q"):
+        inp[key] = torch.stack([inp[key][b, n - T : n] for b, n in enumerate(lens)]).contiguous()
+    return Workload(**{**full.__dict__, "n_q": T, "q_pos0": cap - T}), inp, lens
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=[e[0] for e in VARLEN])
+def test_decode_varlen_batch(case):
+    wl, cpu, lens = _varlen_case(case)
+    g = _to(cpu, DEV)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    res = dsa.forward_varlen(g["qidx"], g["w"], g["kidx"], g["q"], g["k"], g["v"], seq, top_k=wl.top_k,
+                             scale=wl.scale, return_mask=True, return_lse=True)
+    torch.cuda.synchronize()
+    T, lp = wl.n_q, dsa.lpad(wl.n_kv)
+    for b, n in enumerate(lens):
+        # against the oracle, sequence by sequence
+        one = Workload(**{**wl.__dict__, "batch": 1, "q_pos0": n - T, "n_kv": n})
+        sub = {k: v[b : b + 1] for k, v in cpu.items()}
+        _check_sequence(one, sub, {k: v[b : b + 1] for k, v in res.items()}, None, 0, range(T),
+                        integer=wl.integer_indexer)
+        # against the same layer run on that sequence alone: identical bits
+        alone = dsa.forward(g["qidx"][b : b + 1], g["w"][b : b + 1], g["kidx"][b : b + 1].contiguous(),
+                            g["q"][b : b + 1], g["k"][b : b + 1].contiguous(), g["v"][b : b + 1].contiguous(),
+                            top_k=wl.top_k, q_pos0=n - T, n_kv=n, scale=wl.scale, return_mask=True,
+                            return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(res["indices"][b], alone["indices"][0])
+        assert torch.equal(res["out"][b], alone["out"][0])
+        assert torch.equal(res["lse"][b], alone["lse"][0])
+        m_alone = alone["mask"][0]
+        assert torch.equal(res["mask"][b, :, : m_alone.shape[-1]], m_alone)
+        assert not res["mask"][b, :, m_alone.shape[-1] :].any()
+    assert res["mask"].shape[-1] == lp // 32
+
+
+def test_decode_varlen_lengths_are_clamped():
+    """Lengths outside [T, n_kv] act as the nearest bound."""
+    wl, cpu, lens = _varlen_case(("varlen_clamp", "bf16", 2, 700, [700, 2, 300], 32, 128, 100, 8, 8, 128, False))
+    g = _to(cpu, DEV)
+    kw = dict(top_k=wl.top_k, scale=wl.scale, return_lse=True)
+    a = dsa.forward_varlen(g["qidx"], g["w"], g["kidx"], g["q"], g["k"], g["v"],
+                           torch.tensor(lens, dtype=torch.int32, device=DEV), **kw)
+    b = dsa.forward_varlen(g["qidx"], g["w"], g["kidx"], g["q"], g["k"], g["v"],
+                           torch.tensor([100000, -5, 300], dtype=torch.int32, device=DEV), **kw)
+    torch.cuda.synchronize()
+    for key in ("out", "lse", "indices"):
+        assert torch.equal(a[key], b[key]), key
