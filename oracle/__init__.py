@@ -14,3 +14,4 @@ from .dsa_oracle import (  # noqa: F401
     round_scores_fp32,
     select_topk,
 )
+from .front_end import indexer_front_end  # noqa: F401,E402
