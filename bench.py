@@ -12,7 +12,9 @@ workload is single-layer prefill of one 4096-token sequence (32x128
 indexer, top_k 2048, 32x128 attention); the batched decode step (64
 sequences x 32768 cached tokens) and the chunked 65536-token prefill are
 measured in the same run and reported under "secondary". Each query is one
-token, so queries/s equals tokens/s.
+token, so queries/s equals tokens/s. The indexer front end (the q_b, k and
+projection products that produce the indexer's inputs) is timed on its own
+prefill and decode shapes and reported under "front_end".
 
 Per-kernel times come from HIP events recorded on the stream the kernels run
 on, around the op-level entry points (dsa_index_scores, dsa_topk_mask,
@@ -55,6 +57,8 @@ def parse():
     ap.add_argument("--secondary", default=",".join(SECONDARY),
                     help="comma-separated workloads also measured ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--front-end-steps", type=int, default=20,
+                    help="calls timed per indexer front-end workload (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle timing on the host (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,6 +234,61 @@ def run_gpu(wl, steps, warmup, torch, dsa, make_inputs):
     }
 
 
+def front_end_work(fw):
+    """Algorithmic flops and HBM bytes of one indexer front-end call: the
+    three products, and every operand read once and every result written
+    once (weights and activations bf16, w float32)."""
+    M = fw.batch * fw.n_q
+    HI, DI = fw.idx_heads, fw.idx_dim
+    flops = 2.0 * M * (HI * DI * fw.q_rank + (DI + HI) * fw.hidden)
+    weights = 2.0 * (HI * DI * fw.q_rank + (DI + HI) * fw.hidden)
+    acts = 2.0 * M * (fw.hidden + fw.q_rank)
+    outs = M * (2.0 * HI * DI + 2.0 * DI + 4.0 * HI)
+    return flops, weights + acts + outs
+
+
+def run_front_end(fw, steps, torch, dsa, make_front_end_inputs):
+    """Times dsa_indexer_project on one front-end workload (HIP events on
+    the stream it runs on; every rep enqueued before the events are read)."""
+    dev = torch.device("cuda:0")
+    g = make_front_end_inputs(fw, dev)
+    d = dsa.make_proj_dims(batch=fw.batch, n_q=fw.n_q, q_pos0=fw.q_pos0, kv_capacity=fw.kv_capacity,
+                           hidden=fw.hidden, q_rank=fw.q_rank, idx_heads=fw.idx_heads, idx_dim=fw.idx_dim)
+    ws = torch.empty(max(dsa.proj_workspace_size(d), 256), dtype=torch.uint8, device=dev)
+    qo = torch.empty((fw.batch, fw.n_q, fw.idx_heads, fw.idx_dim), dtype=torch.bfloat16, device=dev)
+    wo = torch.empty((fw.batch, fw.n_q, fw.idx_heads), dtype=torch.float32, device=dev)
+
+    def call():
+        dsa.indexer_project(g["x"], g["q_lat"], g["w_qb"], g["w_k"], g["w_proj"], g["kidx_cache"],
+                            q_pos0=fw.q_pos0, workspace=ws, qidx_out=qo, w_out=wo)
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops, nbytes = front_end_work(fw)
+    M = fw.batch * fw.n_q
+    tflops, gbs = flops / (ms * 1e-3) / 1e12, nbytes / (ms * 1e-3) / 1e9
+    # the bound is whichever roofline time is longer
+    mfma_bound = flops / (PEAK_BF16_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
+    roof = ({"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(tflops / PEAK_BF16_TFLOPS, 4)} if mfma_bound else
+            {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    del g, ws, qo, wo
+    torch.cuda.empty_cache()
+    return {"workload": fw.name, "ms_per_call": round(ms, 5), "tokens_per_s": M / (ms * 1e-3),
+            "flop_per_call": flops, "bytes_per_call": nbytes, "roofline": roof,
+            "kernel": "proj_gemm_kernel (+ proj_reduce_kernel for K-split products)"}
+
+
 # ----------------------------------------------------------------------------- CPU oracle timing
 
 def cpu_baseline(wl, budget_s, torch, make_inputs):
@@ -282,7 +341,7 @@ def main():
     import torch
 
     import dsa_lightning_indexer_03_amd as dsa
-    from dsa_workloads import WORKLOADS, make_inputs
+    from dsa_workloads import FRONT_END_WORKLOADS, WORKLOADS, make_front_end_inputs, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -301,6 +360,13 @@ def main():
             "ms_per_step": round(r["ms_per_step"], 4), "steps": args.secondary_steps,
             "roofline": _roofline(r["dominant"], name), "kernels": r["kernels"],
         })
+    front_end = []
+    if args.front_end_steps > 0:
+        for fw in FRONT_END_WORKLOADS.values():
+            r = run_front_end(fw, args.front_end_steps, torch, dsa, make_front_end_inputs)
+            log(f"[bench] {fw.name}: {1e3 * r['ms_per_call']:.1f} us/call, "
+                f"{r['roofline']['achieved']} {r['roofline']['unit']}")
+            front_end.append(r)
     if args.copy_calibration:
         # one plain streaming kernel of known size (2^28 float32: 1 GiB read,
         # 1 GiB written) as the reference reading for the HBM byte counters
@@ -337,6 +403,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": head["kernels"],
         "secondary": secondary,
+        "front_end": front_end,
         "device": torch.cuda.get_device_name(0),
     }
     text = json.dumps(line)

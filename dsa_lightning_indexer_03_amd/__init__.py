@@ -9,7 +9,7 @@ library is missing or a tensor is not on the GPU, calls raise.
 
 Entry points (same names as the C ABI, without the prefix):
   index_scores, topk_mask, sparse_attention, forward, forward_varlen,
-  workspace_size
+  indexer_project, workspace_size
 """
 from __future__ import annotations
 
@@ -22,7 +22,8 @@ import torch  # imported before libdsa.so so both resolve to one HIP runtime
 __all__ = [
     "DsaError", "DSA_OP_INDEX_SCORES", "DSA_OP_TOPK_MASK", "DSA_OP_SPARSE_ATTENTION",
     "DSA_OP_FORWARD", "library_path", "lib", "make_dims", "index_scores", "topk_mask",
-    "sparse_attention", "forward", "forward_varlen", "workspace_size", "lpad",
+    "sparse_attention", "forward", "forward_varlen", "indexer_project", "ProjDims",
+    "make_proj_dims", "proj_workspace_size", "workspace_size", "lpad",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,14 @@ class Dims(ctypes.Structure):
     ]
 
 
+class ProjDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q", ctypes.c_int32), ("q_pos0", ctypes.c_int32),
+        ("kv_capacity", ctypes.c_int32), ("hidden", ctypes.c_int32), ("q_rank", ctypes.c_int32),
+        ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.c_void_p
 _SIGS = {
     "dsa_index_scores": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P]),
@@ -58,6 +67,9 @@ _SIGS = {
                                    _P, ctypes.c_size_t, _P]),
     "dsa_forward_varlen": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, ctypes.c_size_t, _P]),
+    "dsa_indexer_project": (ctypes.c_int, [ctypes.POINTER(ProjDims), _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, ctypes.c_size_t, _P]),
+    "dsa_indexer_project_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ProjDims)]),
     "dsa_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Dims), ctypes.c_int32]),
     "dsa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "dsa_last_error": (ctypes.c_char_p, []),
@@ -267,3 +279,52 @@ def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
 def forward_varlen(qidx, w, kidx, q, k, v, seq_lens, *, top_k, **kw):
     """forward() for a decode batch of different sequence lengths (see there)."""
     return forward(qidx, w, kidx, q, k, v, top_k=top_k, seq_lens=seq_lens, **kw)
+
+
+def make_proj_dims(*, batch, n_q, q_pos0, kv_capacity, hidden, q_rank, idx_heads, idx_dim) -> ProjDims:
+    return ProjDims(batch, n_q, q_pos0, kv_capacity, hidden, q_rank, idx_heads, idx_dim)
+
+
+def proj_workspace_size(dims: ProjDims) -> int:
+    return int(lib().dsa_indexer_project_workspace_size(ctypes.byref(dims)))
+
+
+def indexer_project(x, q_lat, w_qb, w_k, w_proj, kidx_cache, *, q_pos0=0, workspace=None,
+                    qidx_out=None, w_out=None):
+    """Indexer front end (bf16): returns (qidx [B, T, H_I, D_I] bf16, w [B, T, H_I]
+    float32) and writes kidx of the T tokens into rows q_pos0 .. q_pos0+T-1 of
+    `kidx_cache` [B, L, D_I] in place. Weights are [out][in]: w_qb
+    [H_I*D_I, q_rank], w_k [D_I, hidden], w_proj [H_I, hidden]."""
+    _need_gpu(x, q_lat, w_qb, w_k, w_proj, kidx_cache, workspace, qidx_out, w_out)
+    B, T, hidden = x.shape
+    q_rank = q_lat.shape[2]
+    HI = w_proj.shape[0]
+    DI = w_k.shape[0]
+    cap = kidx_cache.shape[1]
+    bf = torch.bfloat16
+    _expect("x", x, (B, T, hidden), bf)
+    _expect("q_lat", q_lat, (B, T, q_rank), bf)
+    _expect("w_qb", w_qb, (HI * DI, q_rank), bf)
+    _expect("w_k", w_k, (DI, hidden), bf)
+    _expect("w_proj", w_proj, (HI, hidden), bf)
+    _expect("kidx_cache", kidx_cache, (B, cap, DI), bf)
+    _expect("qidx_out", qidx_out, (B, T, HI, DI), bf)
+    _expect("w_out", w_out, (B, T, HI), torch.float32)
+    d = make_proj_dims(batch=B, n_q=T, q_pos0=q_pos0, kv_capacity=cap, hidden=hidden, q_rank=q_rank,
+                       idx_heads=HI, idx_dim=DI)
+    qidx = qidx_out if qidx_out is not None else torch.empty((B, T, HI, DI), dtype=bf, device=x.device)
+    w = w_out if w_out is not None else torch.empty((B, T, HI), dtype=torch.float32, device=x.device)
+    need = proj_workspace_size(d)
+    ws, nbytes = None, 0
+    if need > 0:
+        if workspace is not None:
+            nbytes = workspace.numel() * workspace.element_size()
+            if nbytes < need:
+                raise ValueError(f"workspace of {nbytes} bytes, need {need}")
+            ws = workspace
+        else:
+            ws, nbytes = torch.empty(need, dtype=torch.uint8, device=x.device), need
+    _check(lib().dsa_indexer_project(ctypes.byref(d), _ptr(x), _ptr(q_lat), _ptr(w_qb), _ptr(w_k),
+                                     _ptr(w_proj), _ptr(qidx), _ptr(w), _ptr(kidx_cache), _ptr(ws),
+                                     nbytes, _stream(x)))
+    return qidx, w

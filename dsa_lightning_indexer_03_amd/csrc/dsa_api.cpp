@@ -290,9 +290,90 @@ dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const 
   return hip_status(dsa::launch_attn_gather(g, d.dtype, d.head_dim, st), "gather attention launch", st);
 }
 
+dsa_status check_proj_dims(const dsa_proj_dims* d) {
+  if (!d) return fail(DSA_ERR_NULL, "dims is NULL");
+  if (d->batch < 1 || d->n_q < 1) return fail(DSA_ERR_SHAPE, "batch (%d) and n_q (%d) must be >= 1", d->batch, d->n_q);
+  if (d->q_pos0 < 0 || (int64_t)d->q_pos0 + d->n_q > d->kv_capacity)
+    return fail(DSA_ERR_SHAPE, "need 0 <= q_pos0 and q_pos0 + n_q (%lld) <= kv_capacity (%d)",
+                (long long)d->q_pos0 + d->n_q, d->kv_capacity);
+  if ((int64_t)d->batch * d->n_q > 65535ll * 128)
+    return fail(DSA_ERR_SHAPE, "batch * n_q (%lld) above %d", (long long)d->batch * d->n_q, 65535 * 128);
+  if (d->hidden < 64 || d->hidden % 64 != 0 || d->q_rank < 64 || d->q_rank % 64 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "hidden (%d) and q_rank (%d) must be positive multiples of 64", d->hidden,
+                d->q_rank);
+  if (d->hidden > (1 << 20) || d->q_rank > (1 << 20)) return fail(DSA_ERR_SHAPE, "hidden / q_rank too large");
+  if (d->idx_heads < 1 || d->idx_heads > 32)
+    return fail(d->idx_heads < 1 ? DSA_ERR_SHAPE : DSA_ERR_UNSUPPORTED, "idx_heads %d not in [1, 32]", d->idx_heads);
+  if (d->idx_dim != 32 && d->idx_dim != 64 && d->idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "idx_dim %d not in {32, 64, 128}", d->idx_dim);
+  return DSA_OK;
+}
+
+size_t proj_ws(const dsa_proj_dims& d) {
+  const int M = d.batch * d.n_q;
+  return std::max(dsa::proj_partial_bytes(M, d.idx_heads * d.idx_dim, d.q_rank),
+                  dsa::proj_partial_bytes(M, d.idx_dim + d.idx_heads, d.hidden));
+}
+
 }  // namespace
 
 extern "C" {
+
+dsa_status dsa_indexer_project(const dsa_proj_dims* dims, const void* x, const void* q_lat, const void* w_qb,
+                               const void* w_k, const void* w_proj, void* qidx, float* w, void* kidx_cache,
+                               void* ws, size_t ws_bytes, void* stream) {
+  DSA_TRY(check_proj_dims(dims));
+  DSA_TRY(check_ptr(x, "x"));
+  DSA_TRY(check_ptr(q_lat, "q_lat"));
+  DSA_TRY(check_ptr(w_qb, "w_qb"));
+  DSA_TRY(check_ptr(w_k, "w_k"));
+  DSA_TRY(check_ptr(w_proj, "w_proj"));
+  DSA_TRY(check_ptr(qidx, "qidx"));
+  DSA_TRY(check_ptr(w, "w"));
+  DSA_TRY(check_ptr(kidx_cache, "kidx_cache"));
+  const dsa_proj_dims& d = *dims;
+  const size_t need = proj_ws(d);
+  if (need > 0) {
+    DSA_TRY(check_ptr(ws, "workspace"));
+    if (ws_bytes < need) return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  dsa::ProjParams q{};
+  q.x = q_lat;
+  q.w0 = w_qb;
+  q.w1 = nullptr;
+  q.M = d.batch * d.n_q;
+  q.N0 = d.idx_heads * d.idx_dim;
+  q.N1 = 0;
+  q.K = d.q_rank;
+  q.mode = 0;
+  q.out_bf16 = qidx;
+  q.partial = need > 0 ? static_cast<float*>(ws) : nullptr;
+  DSA_TRY(hip_status(dsa::launch_proj(q, ws_bytes, st), "q_b projection launch", st));
+  dsa::ProjParams k{};
+  k.x = x;
+  k.w0 = w_k;
+  k.w1 = w_proj;
+  k.M = d.batch * d.n_q;
+  k.N0 = d.idx_dim;
+  k.N1 = d.idx_heads;
+  k.K = d.hidden;
+  k.mode = 1;
+  k.out_bf16 = kidx_cache;
+  k.out_f32 = w;
+  k.T = d.n_q;
+  k.q_pos0 = d.q_pos0;
+  k.kv_cap = d.kv_capacity;
+  k.partial = need > 0 ? static_cast<float*>(ws) : nullptr;
+  DSA_TRY(hip_status(dsa::launch_proj(k, ws_bytes, st), "k / projection launch", st));
+  return ok();
+}
+
+size_t dsa_indexer_project_workspace_size(const dsa_proj_dims* dims) {
+  if (check_proj_dims(dims) != DSA_OK) return 0;
+  return proj_ws(*dims);
+}
+
 
 dsa_status dsa_index_scores(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
                             float* scores, void* stream) {

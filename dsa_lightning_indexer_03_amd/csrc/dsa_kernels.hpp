@@ -19,6 +19,25 @@ struct IndexerParams {
 };
 hipError_t launch_indexer(const IndexerParams& p, int dtype, int DI, hipStream_t st);
 
+// Indexer front end: one product C = X W^T (bf16 in, float32 accumulate),
+// W the rows of w0 (outputs 0..N0-1) followed by those of w1 (N0..N0+N1-1).
+struct ProjParams {
+  const void* x;      // [M][K] bf16, token rows m = b * T + t
+  const void* w0;     // [N0][K] bf16
+  const void* w1;     // [N1][K] bf16 (mode 1), may be nullptr when N1 == 0
+  int M, N0, N1, K;
+  int mode;           // 0: out_bf16 = qidx [M][N0]; 1: out_bf16 = index-key cache rows, out_f32 = w [M][N1]
+  void* out_bf16;
+  float* out_f32;
+  int T, q_pos0, kv_cap;  // mode 1: token m goes to cache row (m / T) * kv_cap + q_pos0 + m % T
+  float* partial;     // K-split float32 partials (workspace) or nullptr: no split
+  int k_split;        // set by the launcher
+};
+// Workspace bytes of the K-split partials launch_proj uses for an M x N x K
+// product (0: no split).
+size_t proj_partial_bytes(int M, int N, int K);
+hipError_t launch_proj(const ProjParams& p, size_t ws_bytes, hipStream_t st);
+
 // Top-k -> bitmask (+ ascending indices).
 struct TopkParams {
   const float* scores;  // [B][T][Lpad]

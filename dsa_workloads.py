@@ -179,3 +179,52 @@ def sample_rows(wl: Workload, n_rows: int, seed: int = 1234):
     rest = [int(r) for r in torch.randperm(T, generator=g).tolist() if r not in must_set]
     rows = must + rest[: max(0, n_rows - len(must))]
     return sorted(rows)
+
+
+@dataclasses.dataclass(frozen=True)
+class FrontEndWorkload:
+    """Shapes of one indexer front-end call. The pages give no model widths;
+    hidden 7168 and q_rank 1536 are synthetic stand-ins of the size of
+    public MLA models of this family."""
+    name: str
+    batch: int
+    n_q: int
+    q_pos0: int
+    kv_capacity: int
+    hidden: int
+    q_rank: int
+    idx_heads: int
+    idx_dim: int
+    seed: int
+    description: str = ""
+
+
+FRONT_END_WORKLOADS = {
+    w.name: w
+    for w in [
+        FrontEndWorkload("front_end_prefill_T4096", 1, 4096, 0, 4096, 7168, 1536, 32, 128, 11,
+                         "indexer front end of the 4096-token prefill"),
+        FrontEndWorkload("front_end_decode_B64", 64, 1, 32767, 32768, 7168, 1536, 32, 128, 12,
+                         "indexer front end of one decode step of 64 sequences"),
+    ]
+}
+
+
+def make_front_end_inputs(wl: FrontEndWorkload, device="cpu", kv_capacity=None):
+    """x, q_lat ~ N(0, 1) and weights ~ N(0, 1/in) (so outputs are O(1)),
+    all rounded to bf16, drawn in that order with torch's seeded generator.
+    The index-key cache is drawn too (rows the call must leave untouched)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    bf = torch.bfloat16
+    B, T, hid, r, HI, DI = wl.batch, wl.n_q, wl.hidden, wl.q_rank, wl.idx_heads, wl.idx_dim
+    cap = wl.kv_capacity if kv_capacity is None else kv_capacity
+    return {
+        "x": _normal((B, T, hid), 1.0, bf, gen, dev),
+        "q_lat": _normal((B, T, r), 1.0, bf, gen, dev),
+        "w_qb": _normal((HI * DI, r), 1.0 / math.sqrt(r), bf, gen, dev),
+        "w_k": _normal((DI, hid), 1.0 / math.sqrt(hid), bf, gen, dev),
+        "w_proj": _normal((HI, hid), 1.0 / math.sqrt(hid), bf, gen, dev),
+        "kidx_cache": _normal((B, cap, DI), 1.0, bf, gen, dev),
+    }

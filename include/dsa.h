@@ -173,6 +173,50 @@ dsa_status dsa_forward_varlen(const dsa_dims* dims, const int32_t* seq_lens, con
                               int32_t* indices, uint32_t* mask, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Problem sizes of the indexer front end (dsa_indexer_project). bf16 only.
+ * Supported: hidden and q_rank multiples of 64; 1 <= idx_heads <= 32;
+ * idx_dim in {32, 64, 128}; q_pos0 + n_q <= kv_capacity. */
+typedef struct {
+  int32_t batch;       /* B: independent sequences                          */
+  int32_t n_q;         /* T: new tokens per sequence in this call           */
+  int32_t q_pos0;      /* cache position of token 0                         */
+  int32_t kv_capacity; /* L: token capacity of the index-key cache          */
+  int32_t hidden;      /* width of the activations x                        */
+  int32_t q_rank;      /* width of the compressed query q_lat               */
+  int32_t idx_heads;   /* H_I                                               */
+  int32_t idx_dim;     /* D_I                                               */
+} dsa_proj_dims;
+
+/* Indexer front end: the indexer's tensors q_b, k and projection [aiu "What
+ * happened"; devotd section 3] applied to T new tokens of B sequences. The
+ * pages name the tensors but give no formula; the reading implemented is
+ * three linear maps (no bias, no norm, no RoPE, no scale):
+ *   qidx[b][t][h][d] = sum_r q_lat[b][t][r] * w_qb[h*idx_dim + d][r]
+ *   kidx_cache[b][q_pos0 + t][d] = sum_j x[b][t][j] * w_k[d][j]
+ *   w[b][t][h] = sum_j x[b][t][j] * w_proj[h][j]
+ * accumulated in float32; qidx and the cache rows are rounded to bf16, w is
+ * float32. The outputs are exactly the inputs dsa_index_scores and
+ * dsa_forward take (qidx, w, kidx with kv_capacity rows per sequence).
+ * Layouts (bf16 unless stated, row-major, batch outermost):
+ *   x [B][T][hidden], q_lat [B][T][q_rank],
+ *   w_qb [idx_heads*idx_dim][q_rank], w_k [idx_dim][hidden],
+ *   w_proj [idx_heads][hidden]             (weights are [out][in]),
+ *   qidx [B][T][idx_heads][idx_dim], w [B][T][idx_heads] float32,
+ *   kidx_cache [B][kv_capacity][idx_dim]: rows q_pos0 .. q_pos0+T-1 of each
+ *   sequence are written, every other row is left untouched.
+ * Needs dsa_indexer_project_workspace_size(dims) bytes of workspace (float32
+ * partial sums of the thin products; `ws` may be NULL when that is 0).
+ * Errors as for the other entry points (DSA_ERR_SHAPE / _UNSUPPORTED for
+ * sizes outside the supported set). */
+dsa_status dsa_indexer_project(const dsa_proj_dims* dims, const void* x, const void* q_lat,
+                               const void* w_qb, const void* w_k, const void* w_proj,
+                               void* qidx, float* w, void* kidx_cache, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Workspace bytes dsa_indexer_project needs for `dims` (0 when none or when
+ * dims are invalid). Host only. */
+size_t dsa_indexer_project_workspace_size(const dsa_proj_dims* dims);
+
 /* Workspace bytes `op` needs for `dims` (0 when none). Returns 0 for invalid
  * dims as well; the op itself then reports the error. Host only. */
 size_t dsa_workspace_size(const dsa_dims* dims, int32_t op);

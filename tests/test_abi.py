@@ -154,3 +154,46 @@ def test_forward_varlen_validation():
     need = dsa.workspace_size(d, dsa.DSA_OP_FORWARD)
     assert need > 0
     assert _varlen(d, ws_bytes=need - 1) == ERR_WORKSPACE
+
+
+def _proj(d, ws=FAKE, ws_bytes=1 << 40, x=FAKE):
+    return dsa.lib().dsa_indexer_project(ctypes.byref(d), x, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                         ws_bytes, None)
+
+
+def _pdims(**kw):
+    base = dict(batch=1, n_q=64, q_pos0=0, kv_capacity=64, hidden=256, q_rank=128, idx_heads=32, idx_dim=128)
+    base.update(kw)
+    return dsa.make_proj_dims(**base)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(n_q=0), ERR_SHAPE),
+        (dict(q_pos0=1), ERR_SHAPE),               # q_pos0 + n_q > kv_capacity
+        (dict(hidden=100), ERR_UNSUPPORTED),
+        (dict(q_rank=0), ERR_UNSUPPORTED),
+        (dict(idx_heads=33), ERR_UNSUPPORTED),
+        (dict(idx_dim=96), ERR_UNSUPPORTED),
+        (dict(batch=65536, n_q=128, kv_capacity=128), ERR_SHAPE),
+    ],
+)
+def test_indexer_project_rejects_bad_dims(kw, status):
+    assert _proj(_pdims(**kw)) == status
+    assert _err() != ""
+    assert dsa.proj_workspace_size(_pdims(**kw)) == 0
+
+
+def test_indexer_project_pointers_and_workspace():
+    d = _pdims(hidden=1024)
+    assert _proj(d, x=None) == ERR_NULL
+    assert _proj(d, x=FAKE + 2) == ERR_MISALIGNED
+    # 64 tokens x 160 outputs over K=1024 is split over K: partials needed
+    need = dsa.proj_workspace_size(d)
+    assert need > 0
+    assert _proj(d, ws=None) == ERR_NULL
+    assert _proj(d, ws_bytes=need - 1) == ERR_WORKSPACE
+    # a 4096-token prefill needs partials only for the thin k / projection product
+    big = _pdims(n_q=4096, kv_capacity=4096, hidden=7168, q_rank=1536)
+    assert dsa.proj_workspace_size(big) == 8 * 4096 * 160 * 4
