@@ -15,3 +15,4 @@ from .dsa_oracle import (  # noqa: F401
     select_topk,
 )
 from .front_end import indexer_front_end  # noqa: F401,E402
+from .fp8_indexer import e4m3_round, index_scores_fp8, quantize_rows_fp8  # noqa: F401,E402
