@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--secondary", default=",".join(SECONDARY),
                     help="comma-separated workloads also measured ('' for none)")
     ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--fp8-study", default=f"{HEADLINE},longctx_bf16_L65536_chunk4096",
+                    help="workloads on which the fp8 indexer reading is timed and its selection "
+                         "compared with bf16 ('' for none)")
     ap.add_argument("--front-end-steps", type=int, default=20,
                     help="calls timed per indexer front-end workload (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -289,6 +292,66 @@ def run_front_end(fw, steps, torch, dsa, make_front_end_inputs):
             "kernel": "proj_gemm_kernel (+ proj_reduce_kernel for K-split products)"}
 
 
+def _popcount32(x, torch):
+    """Set bits per int32 word (as int64)."""
+    v = x.to(torch.int64) & 0xFFFFFFFF
+    v = v - ((v >> 1) & 0x55555555)
+    v = (v & 0x33333333) + ((v >> 2) & 0x33333333)
+    v = (v + (v >> 4)) & 0x0F0F0F0F
+    return (v * 0x01010101 & 0xFFFFFFFF) >> 24
+
+
+def fp8_indexer_study(wl, reps, torch, dsa, make_inputs):
+    """The fp8 (e4m3, per-row scale) reading of the indexer on a workload:
+    indexer time per step against the bf16 indexer (HIP events on the
+    stream), and how much of the bf16 selection the fp8 selection keeps
+    (per query row: kept tokens in both / kept tokens of bf16)."""
+    dev = torch.device("cuda:0")
+    g = make_inputs(wl, dev)
+    calls = chunk_calls(wl)
+    stream = torch.cuda.current_stream(dev)
+    k8, ks = dsa.quantize_keys_fp8(g["kidx"], pos0=0, count=wl.n_kv)
+    recall = []
+    t_bf16 = t_fp8 = t_quant = 0.0
+    for (q0, nq, nkv) in calls:
+        sl = slice(q0 - wl.q_pos0, q0 - wl.q_pos0 + nq)
+        qi, wi = g["qidx"][:, sl], g["w"][:, sl]
+        sc = dsa.index_scores(qi, wi, g["kidx"], q_pos0=q0, n_kv=nkv)
+        mb, _ = dsa.topk_mask(sc, q_pos0=q0, n_kv=nkv, top_k=wl.top_k, indices=False)
+        q8, wq = dsa.quantize_fp8(qi.contiguous(), wi.contiguous())
+        sc8 = dsa.index_scores_fp8(q8, wq, k8, ks, q_pos0=q0, n_kv=nkv, out=sc)
+        m8, _ = dsa.topk_mask(sc8, q_pos0=q0, n_kv=nkv, top_k=wl.top_k, indices=False)
+        both = _popcount32(mb & m8, torch).sum(-1)
+        recall.append((both.double() / _popcount32(mb, torch).sum(-1).double()).flatten())
+        del mb, m8
+        qic, wic = qi.contiguous(), wi.contiguous()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        for _ in range(reps):
+            dsa.index_scores(qi, wi, g["kidx"], q_pos0=q0, n_kv=nkv, out=sc)
+        ev[1].record(stream)
+        for _ in range(reps):
+            dsa.quantize_fp8(qic, wic)
+        ev[2].record(stream)
+        for _ in range(reps):
+            dsa.index_scores_fp8(q8, wq, k8, ks, q_pos0=q0, n_kv=nkv, out=sc)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        t_bf16 += ev[0].elapsed_time(ev[1]) / reps
+        t_quant += ev[1].elapsed_time(ev[2]) / reps
+        t_fp8 += ev[2].elapsed_time(ev[3]) / reps
+        del sc, sc8
+    r = torch.cat(recall)
+    out = {"workload": wl.name, "bf16_index_ms_per_step": round(t_bf16, 4),
+           "fp8_index_ms_per_step": round(t_fp8, 4), "fp8_query_quantize_ms_per_step": round(t_quant, 4),
+           "indexer_speedup": round(t_bf16 / t_fp8, 3), "rows": int(r.numel()),
+           "selection_recall_mean": round(r.mean().item(), 5), "selection_recall_min": round(r.min().item(), 5),
+           "selection_recall_p01": round(torch.quantile(r.float().cpu(), 0.01).item(), 5)}
+    del g, k8, ks
+    torch.cuda.empty_cache()
+    return out
+
+
 # ----------------------------------------------------------------------------- CPU oracle timing
 
 def cpu_baseline(wl, budget_s, torch, make_inputs):
@@ -367,6 +430,12 @@ def main():
             log(f"[bench] {fw.name}: {1e3 * r['ms_per_call']:.1f} us/call, "
                 f"{r['roofline']['achieved']} {r['roofline']['unit']}")
             front_end.append(r)
+    fp8_study = []
+    for name in [s_ for s_ in args.fp8_study.split(",") if s_]:
+        r = fp8_indexer_study(WORKLOADS[name], 3, torch, dsa, make_inputs)
+        log(f"[bench] fp8 indexer on {name}: {r['fp8_index_ms_per_step']} ms vs bf16 "
+            f"{r['bf16_index_ms_per_step']} ms, recall mean {r['selection_recall_mean']}")
+        fp8_study.append(r)
     if args.copy_calibration:
         # one plain streaming kernel of known size (2^28 float32: 1 GiB read,
         # 1 GiB written) as the reference reading for the HBM byte counters
@@ -404,6 +473,7 @@ def main():
         "kernels": head["kernels"],
         "secondary": secondary,
         "front_end": front_end,
+        "fp8_indexer": fp8_study,
         "device": torch.cuda.get_device_name(0),
     }
     text = json.dumps(line)

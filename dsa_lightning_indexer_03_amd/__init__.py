@@ -9,7 +9,8 @@ library is missing or a tensor is not on the GPU, calls raise.
 
 Entry points (same names as the C ABI, without the prefix):
   index_scores, topk_mask, sparse_attention, forward, forward_varlen,
-  indexer_project, workspace_size
+  indexer_project, quantize_fp8, quantize_keys_fp8, index_scores_fp8,
+  workspace_size
 """
 from __future__ import annotations
 
@@ -23,7 +24,8 @@ __all__ = [
     "DsaError", "DSA_OP_INDEX_SCORES", "DSA_OP_TOPK_MASK", "DSA_OP_SPARSE_ATTENTION",
     "DSA_OP_FORWARD", "library_path", "lib", "make_dims", "index_scores", "topk_mask",
     "sparse_attention", "forward", "forward_varlen", "indexer_project", "ProjDims",
-    "make_proj_dims", "proj_workspace_size", "workspace_size", "lpad",
+    "make_proj_dims", "proj_workspace_size", "quantize_fp8", "quantize_keys_fp8", "index_scores_fp8",
+    "workspace_size", "lpad",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +69,8 @@ _SIGS = {
                                    _P, ctypes.c_size_t, _P]),
     "dsa_forward_varlen": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, ctypes.c_size_t, _P]),
+    "dsa_quantize_fp8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dsa_index_scores_fp8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P]),
     "dsa_indexer_project": (ctypes.c_int, [ctypes.POINTER(ProjDims), _P, _P, _P, _P, _P, _P, _P, _P,
                                            _P, ctypes.c_size_t, _P]),
     "dsa_indexer_project_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(ProjDims)]),
@@ -328,3 +332,73 @@ def indexer_project(x, q_lat, w_qb, w_k, w_proj, kidx_cache, *, q_pos0=0, worksp
                                      _ptr(w_proj), _ptr(qidx), _ptr(w), _ptr(kidx_cache), _ptr(ws),
                                      nbytes, _stream(x)))
     return qidx, w
+
+
+def quantize_fp8(qidx, w, kidx=None, *, q_pos0=0, kidx8=None, kscale=None):
+    """e4m3 quantisation of the indexer's queries (qidx [B, T, H_I, 128] bf16,
+    w [B, T, H_I] float32) -> (qidx8 uint8 [B, T, H_I, 128], wq [B, T, H_I]),
+    one scale per head row folded into wq. With `kidx` [B, L, 128] also
+    quantises its rows q_pos0 .. q_pos0+T-1 (the call's tokens) into `kidx8`
+    [B, L, 128] uint8 and `kscale` [B, L] float32 (allocated zero-filled when
+    not given) and returns (qidx8, wq, kidx8, kscale)."""
+    _need_gpu(qidx, w, kidx, kidx8, kscale)
+    B, T, HI, DI = qidx.shape
+    _expect("w", w, (B, T, HI), torch.float32)
+    qidx8 = torch.empty((B, T, HI, DI), dtype=torch.uint8, device=qidx.device)
+    wq = torch.empty((B, T, HI), dtype=torch.float32, device=qidx.device)
+    cap = T + q_pos0
+    if kidx is not None:
+        cap = kidx.shape[1]
+        _expect("kidx", kidx, (B, cap, DI), qidx.dtype)
+        if kidx8 is None:
+            kidx8 = torch.zeros((B, cap, DI), dtype=torch.uint8, device=qidx.device)
+        if kscale is None:
+            kscale = torch.zeros((B, cap), dtype=torch.float32, device=qidx.device)
+        _expect("kidx8", kidx8, (B, cap, DI), torch.uint8)
+        _expect("kscale", kscale, (B, cap), torch.float32)
+    d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=cap, kv_capacity=cap, idx_heads=HI, idx_dim=DI,
+                  dtype=_dtype_code(qidx))
+    _check(lib().dsa_quantize_fp8(ctypes.byref(d), _ptr(qidx), _ptr(w), _ptr(kidx), _ptr(qidx8), _ptr(wq),
+                                  _ptr(kidx8 if kidx is not None else None),
+                                  _ptr(kscale if kidx is not None else None), _stream(qidx)))
+    return (qidx8, wq) if kidx is None else (qidx8, wq, kidx8, kscale)
+
+
+def quantize_keys_fp8(kidx, *, pos0=0, count=None, kidx8=None, kscale=None):
+    """e4m3 quantisation of key rows pos0 .. pos0+count-1 (default: all) of
+    kidx [B, L, 128] bf16 into kidx8 [B, L, 128] uint8 and kscale [B, L]."""
+    _need_gpu(kidx, kidx8, kscale)
+    B, cap, DI = kidx.shape
+    count = cap - pos0 if count is None else count
+    if kidx8 is None:
+        kidx8 = torch.zeros((B, cap, DI), dtype=torch.uint8, device=kidx.device)
+    if kscale is None:
+        kscale = torch.zeros((B, cap), dtype=torch.float32, device=kidx.device)
+    _expect("kidx8", kidx8, (B, cap, DI), torch.uint8)
+    _expect("kscale", kscale, (B, cap), torch.float32)
+    d = make_dims(batch=B, n_q=count, q_pos0=pos0, n_kv=cap, kv_capacity=cap, idx_heads=1, idx_dim=DI,
+                  dtype=_dtype_code(kidx))
+    _check(lib().dsa_quantize_fp8(ctypes.byref(d), None, None, _ptr(kidx), None, None, _ptr(kidx8),
+                                  _ptr(kscale), _stream(kidx)))
+    return kidx8, kscale
+
+
+def index_scores_fp8(qidx8, wq, kidx8, kscale, *, q_pos0=0, n_kv=None, out=None):
+    """fp8 indexer scores [B, T, Lpad] float32 (-inf for s > p) from the
+    quantised tensors of quantize_fp8 / quantize_keys_fp8."""
+    _need_gpu(qidx8, wq, kidx8, kscale, out)
+    B, T, HI, DI = qidx8.shape
+    cap = kidx8.shape[1]
+    n_kv = cap if n_kv is None else n_kv
+    _expect("qidx8", qidx8, (B, T, HI, DI), torch.uint8)
+    _expect("wq", wq, (B, T, HI), torch.float32)
+    _expect("kidx8", kidx8, (B, cap, DI), torch.uint8)
+    _expect("kscale", kscale, (B, cap), torch.float32)
+    _expect("out", out, (B, T, lpad(n_kv)), torch.float32)
+    d = make_dims(batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, kv_capacity=cap, idx_heads=HI, idx_dim=DI,
+                  dtype=DSA_BF16)
+    if out is None:
+        out = torch.empty((B, T, lpad(n_kv)), dtype=torch.float32, device=qidx8.device)
+    _check(lib().dsa_index_scores_fp8(ctypes.byref(d), _ptr(qidx8), _ptr(wq), _ptr(kidx8), _ptr(kscale),
+                                      _ptr(out), _stream(qidx8)))
+    return out

@@ -17,11 +17,19 @@ constexpr float kLazyMax = 8.0f;             // log2 units
 constexpr float kLn2f = 0.69314718055994530942f;
 
 // Swizzle of a key row's 16-byte columns: physical column = col ^ swz(row).
-// swz is a bijection on row mod 16 (so the 16 rows a K fragment read touches
-// land in 16 different columns) and, within every aligned group of four
-// rows, differs in its upper three bits (so the four rows x two columns a
-// 16-lane transpose read touches land in eight different columns).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1) | (row & 8); }
+// LDS serves 256 bytes (64 four-byte banks) per pass, so the 16-byte pieces
+// that 16 lanes of a K fragment read (16 rows, one column) and that 32 lanes
+// of a V^T transpose read (two groups of four rows, two columns each) must
+// all fall in different 16-byte slots of a 256-byte window. swz is a
+// bijection on row mod 16 (the K read); within an aligned group of four rows
+// its bits 1-2 take all four values (eight slots for one 16-lane group of the
+// transpose read), and bit 3 is row bit 2 ^ row bit 3, so the neighbouring
+// group of four rows lands in the other eight slots. (Bit 3 equal to row
+// bit 3 alone put both groups in the same slots: a two-way conflict on
+// every transpose read, measured as half of the kernel's LDS cycles.)
+__device__ __forceinline__ int swz(int row) {
+  return ((row & 3) << 1) | ((row >> 2) & 1) | ((((row >> 2) ^ (row >> 3)) & 1) << 3);
+}
 // Byte offset of 16-byte column `col` of key row `row` in a swizzled tile.
 __device__ __forceinline__ int tile_off(int row, int col) { return row * kRow + ((col ^ swz(row)) << 4); }
 

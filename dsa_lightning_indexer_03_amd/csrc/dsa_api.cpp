@@ -369,6 +369,75 @@ dsa_status dsa_indexer_project(const dsa_proj_dims* dims, const void* x, const v
   return ok();
 }
 
+dsa_status dsa_quantize_fp8(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
+                            uint8_t* qidx8, float* wq, uint8_t* kidx8, float* kscale, void* stream) {
+  DSA_TRY(check_dims(dims, true, false, false));
+  const dsa_dims& d = *dims;
+  if (d.dtype != DSA_BF16 || d.idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "fp8 indexer needs bf16 inputs with idx_dim 128 (dtype %d, idx_dim %d)", d.dtype,
+                d.idx_dim);
+  const bool do_q = qidx || w || qidx8 || wq, do_k = kidx || kidx8 || kscale;
+  if (!do_q && !do_k) return fail(DSA_ERR_NULL, "nothing to quantise (queries and keys both NULL)");
+  if (do_q) {
+    DSA_TRY(check_ptr(qidx, "qidx"));
+    DSA_TRY(check_ptr(w, "w"));
+    DSA_TRY(check_ptr(qidx8, "qidx8"));
+    DSA_TRY(check_ptr(wq, "wq"));
+  }
+  if (do_k) {
+    DSA_TRY(check_ptr(kidx, "kidx"));
+    DSA_TRY(check_ptr(kidx8, "kidx8"));
+    DSA_TRY(check_ptr(kscale, "kscale"));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  dsa::QuantParams p{};
+  p.qidx = do_q ? qidx : nullptr;
+  p.w = w;
+  p.kidx = do_k ? kidx : nullptr;
+  p.qidx8 = qidx8;
+  p.wq = wq;
+  p.kidx8 = kidx8;
+  p.kscale = kscale;
+  p.B = d.batch;
+  p.T = d.n_q;
+  p.q_pos0 = d.q_pos0;
+  p.kv_cap = d.kv_capacity;
+  p.HI = d.idx_heads;
+  DSA_TRY(hip_status(dsa::launch_quantize_fp8(p, st), "fp8 quantisation launch", st));
+  return ok();
+}
+
+dsa_status dsa_index_scores_fp8(const dsa_dims* dims, const uint8_t* qidx8, const float* wq, const uint8_t* kidx8,
+                                const float* kscale, float* scores, void* stream) {
+  DSA_TRY(check_dims(dims, true, false, false));
+  const dsa_dims& d = *dims;
+  if (d.dtype != DSA_BF16 || d.idx_dim != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "fp8 indexer needs bf16 inputs with idx_dim 128 (dtype %d, idx_dim %d)", d.dtype,
+                d.idx_dim);
+  DSA_TRY(check_ptr(qidx8, "qidx8"));
+  DSA_TRY(check_ptr(wq, "wq"));
+  DSA_TRY(check_ptr(kidx8, "kidx8"));
+  DSA_TRY(check_ptr(kscale, "kscale"));
+  DSA_TRY(check_ptr(scores, "scores"));
+  hipStream_t st = (hipStream_t)stream;
+  dsa::IndexerParams p{};
+  p.qidx = qidx8;
+  p.w = wq;
+  p.kidx = kidx8;
+  p.kscale = kscale;
+  p.scores = scores;
+  p.B = d.batch;
+  p.T = d.n_q;
+  p.q_pos0 = d.q_pos0;
+  p.n_kv = d.n_kv;
+  p.kv_cap = d.kv_capacity;
+  p.HI = d.idx_heads;
+  p.Lpad = (int)lpad_of(d);
+  p.write_upper = 1;
+  DSA_TRY(hip_status(dsa::launch_indexer(p, dsa::kIndexerFp8, 128, st), "fp8 indexer launch", st));
+  return ok();
+}
+
 size_t dsa_indexer_project_workspace_size(const dsa_proj_dims* dims) {
   if (check_proj_dims(dims) != DSA_OK) return 0;
   return proj_ws(*dims);

@@ -26,10 +26,27 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// One e4m3 code (1 sign, 4 exponent, 3 mantissa bits): the storage type of
+// the fp8 indexer's queries and keys.
+struct fp8e4m3 {
+  uint8_t bits;
+};
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; };
 template <> struct Frag<float> { typedef f32x8 type; };
+template <> struct Frag<fp8e4m3> { typedef i32x8 type; };
 template <typename T> using frag_t = typename Frag<T>::type;
+
+// Reduction indices one k-step covers: 32 for bf16 and fp32, 128 for fp8
+// (one v_mfma_scale_f32_16x16x128_f8f6f4). Lane group g = l/16 owns a quarter
+// of them; frag_off is the first element lane group g holds in k-step kk.
+template <typename T> inline constexpr int kStepElems = 32;
+template <> inline constexpr int kStepElems<fp8e4m3> = 128;
+template <typename T> __device__ __forceinline__ int frag_off(int kk, int g) {
+  return kStepElems<T> * kk + (kStepElems<T> / 4) * g;
+}
 
 // 8 contiguous elements (16 B for bf16, 32 B for fp32) from 16-B aligned memory.
 template <typename T> __device__ __forceinline__ frag_t<T> load_frag(const T* p);
@@ -42,11 +59,24 @@ template <> __device__ __forceinline__ f32x8 load_frag<float>(const float* p) {
   return f32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+template <> __device__ __forceinline__ i32x8 load_frag<fp8e4m3>(const fp8e4m3* p) {  // 32 codes, 32-B aligned
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 template <typename T> __device__ __forceinline__ frag_t<T> zero_frag() { return frag_t<T>{}; }
 
 // acc += A(16 x 32) * B(32 x 16) for one k-step.
 __device__ __forceinline__ f32x4 mma_kstep(const bf16x8& a, const bf16x8& b, f32x4 acc) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+// fp8: A 16 x 128, B 128 x 16, e4m3 codes with unit scales (exponent byte
+// 127). Lane l holds 32 codes of row (A) or column (B) l % 16; A and B use
+// the same assignment of reduction indices to lanes, which is all a dot
+// product needs (checked against a CPU product on an MI355X).
+__device__ __forceinline__ f32x4 mma_kstep(const i32x8& a, const i32x8& b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
 }
 __device__ __forceinline__ f32x4 mma_kstep(const f32x8& a, const f32x8& b, f32x4 acc) {
 #pragma unroll

@@ -16,8 +16,26 @@ struct IndexerParams {
   int key_chunk;      // keys per workgroup (multiple of 64)
   int write_upper;    // 1: write -inf for s > p; 0: leave those entries untouched
   const int32_t* seq_len;  // [B] per-sequence cache lengths (decode kernel only), or nullptr
+  const float* kscale;     // fp8 keys: [B][kv_cap] per-key scales; nullptr otherwise
 };
+// dtype: 0 fp32, 1 bf16, kIndexerFp8 e4m3 codes (qidx, kidx; w holds the
+// query-scaled weights, kscale the key scales; DI 128 only)
+constexpr int kIndexerFp8 = 2;
 hipError_t launch_indexer(const IndexerParams& p, int dtype, int DI, hipStream_t st);
+
+// Per-row e4m3 quantisation (rows of 128 bf16 values): scale = max|x| / 448
+// (1 for a zero row), code = e4m3(x / scale), round to nearest even.
+struct QuantParams {
+  const void* qidx;   // [B][T][HI][128] bf16, or nullptr (keys only)
+  const float* w;     // [B][T][HI]
+  const void* kidx;   // [B][kv_cap][128] bf16, or nullptr (queries only); rows q_pos0..q_pos0+T-1
+  uint8_t* qidx8;     // [B][T][HI][128]
+  float* wq;          // [B][T][HI] = w * query scale
+  uint8_t* kidx8;     // [B][kv_cap][128], same rows as kidx
+  float* kscale;      // [B][kv_cap]
+  int B, T, q_pos0, kv_cap, HI;
+};
+hipError_t launch_quantize_fp8(const QuantParams& p, hipStream_t st);
 
 // Indexer front end: one product C = X W^T (bf16 in, float32 accumulate),
 // W the rows of w0 (outputs 0..N0-1) followed by those of w1 (N0..N0+N1-1).

@@ -38,8 +38,8 @@ __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__flo
 
 template <typename T, int DI, int NQ>
 struct QueryFrags {
-  static constexpr int KSTEPS = DI / 32;
-  frag_t<T> a[NQ][2][KSTEPS];  // A operands: heads 16*rb + (l%16), dims 32*kk + 8*(l/16) + e
+  static constexpr int KSTEPS = DI / kStepElems<T>;
+  frag_t<T> a[NQ][2][KSTEPS];  // A operands: heads 16*rb + (l%16), dims frag_off(kk, l/16) + e
   float w[NQ][2][4];           // weights of the heads this lane's accumulators hold
 };
 
@@ -61,7 +61,7 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
       const int head = min(16 * rb + c, a.HI - 1);
 #pragma unroll
       for (int kk = 0; kk < QueryFrags<T, DI, NQ>::KSTEPS; ++kk)
-        f.a[j][rb][kk] = load_frag<T>(qb + ((size_t)tc * a.HI + head) * DI + 32 * kk + 8 * g);
+        f.a[j][rb][kk] = load_frag<T>(qb + ((size_t)tc * a.HI + head) * DI + frag_off<T>(kk, g));
       // weights of heads 16*rb + 4*g + (0..3)
 #pragma unroll
       for (int r = 0; r < 4; ++r) wr[j][rb][r] = wb[(size_t)tc * a.HI + min(16 * rb + 4 * g + r, a.HI - 1)];
@@ -84,14 +84,14 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
 // computed unconditionally, the 2*NQ accumulator chains interleaved per k-step.
 template <typename T, int DI, int NQ>
 __device__ __forceinline__ float score_subtile(const QueryFrags<T, DI, NQ>& f,
-                                               const frag_t<T> (&bf)[DI / 32]) {
+                                               const frag_t<T> (&bf)[DI / kStepElems<T>]) {
   f32x4 acc[NQ][2];
 #pragma unroll
   for (int j = 0; j < NQ; ++j)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) acc[j][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kk = 0; kk < DI / 32; ++kk) {
+  for (int kk = 0; kk < DI / kStepElems<T>; ++kk) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j)
 #pragma unroll
@@ -198,12 +198,22 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void dma16(const void* src, unsigned char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave_base, 16, 0, 0);
 }
+// The same with 4 bytes per lane (lane l's word lands at lds_wave_base + 4 l).
+__device__ __forceinline__ void dma4(const void* src, unsigned char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave_base, 4, 0, 0);
+}
 
 // B fragment (elements 32 kk + 8 g .. +7) of a key row stored with its
 // 16-byte chunks permuted by XOR with sw.
 template <typename T> __device__ __forceinline__ frag_t<T> lds_frag(const unsigned char* rowp, int kk, int g, int sw);
 template <> __device__ __forceinline__ bf16x8 lds_frag<bf16>(const unsigned char* rowp, int kk, int g, int sw) {
   return *reinterpret_cast<const bf16x8*>(rowp + (((4 * kk + g) ^ sw) << 4));
+}
+template <> __device__ __forceinline__ i32x8 lds_frag<fp8e4m3>(const unsigned char* rowp, int kk, int g, int sw) {
+  // codes 128 kk + 32 g .. +31: 16-byte chunks 8 kk + 2 g and 8 kk + 2 g + 1
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(rowp + (((8 * kk + 2 * g) ^ sw) << 4));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(rowp + (((8 * kk + 2 * g + 1) ^ sw) << 4));
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 template <> __device__ __forceinline__ f32x8 lds_frag<float>(const unsigned char* rowp, int kk, int g, int sw) {
   const f32x4 lo = *reinterpret_cast<const f32x4*>(rowp + (((8 * kk + 2 * g) ^ sw) << 4));
@@ -238,11 +248,17 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 template <typename T, int DI>
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a, UnitMap um,
                                                                           long long n_units) {
-  constexpr int KT = kIdxKT, KSTEPS = DI / 32, NSUB = KT / 16, S = kIdxStages;
+  constexpr int KT = kIdxKT, KSTEPS = DI / kStepElems<T>, NSUB = KT / 16, S = kIdxStages;
   constexpr int ROWB = DI * (int)sizeof(T), CH16 = ROWB / 16;
   constexpr int TILEB = KT * ROWB, NINST = TILEB / 1024;  // 1 KiB (64 lanes x 16 B) per instruction
   static_assert(TILEB % 1024 == 0 && (CH16 & (CH16 - 1)) == 0, "tile layout");
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[S * TILEB];
+  // fp8 keys carry one float32 scale per key: every wave keeps its own copy
+  // of the tile's 64 scales after the key rows (so every wave issues the
+  // same number of loads per tile and waits for its own)
+  constexpr bool kFp8 = kStepElems<T> == 128;
+  constexpr int SLOT = TILEB + (kFp8 ? 256 * kIdxWaves : 0);
+  static_assert(!kFp8 || KT == 64, "one 4-byte scale per lane per tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[S * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   // Workgroups are dealt to the 8 XCDs round-robin; the 1/8 of the unit
@@ -263,6 +279,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   // key: finite data whose scores are never stored.
   constexpr int NJ = (NINST + kIdxWaves - 1) / kIdxWaves;
   constexpr bool kAllWavesLoad = NINST % kIdxWaves == 0;
+  constexpr int NLD = NJ + (kFp8 ? 1 : 0);  // loads per wave per tile
   static_assert(kAllWavesLoad || NINST < kIdxWaves, "tile loads split evenly or fit in one round");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);  // wave-uniform copy, kept in a scalar register
   uint32_t dl_off[NJ];  // byte offset of this lane's 16 bytes from the tile's first key row
@@ -277,7 +294,8 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   auto dload = [&](int b, int kt, int slot) {
     const int s0 = kt * KT;
     const char* kb = kcache + ((size_t)b * a.kv_cap + s0) * ROWB;
-    unsigned char* dst = lds + slot * TILEB;
+    unsigned char* dst = lds + slot * SLOT;
+    if constexpr (kFp8) dma4(a.kscale + (size_t)b * a.kv_cap + min(s0 + lane, a.n_kv - 1), dst + TILEB + wave_u * 256);
     if (s0 + KT <= a.n_kv) {
 #pragma unroll
       for (int n = 0; n < NJ; ++n) {
@@ -296,7 +314,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   // B operand of key subtile sub: row 16 sub + c, elements 32 kk + 8 g .. +7
   auto load_b = [&](int slot, int sub, frag_t<T> (&bf)[KSTEPS]) {
     const int row = sub * 16 + c;
-    const unsigned char* rowp = lds + slot * TILEB + row * ROWB;
+    const unsigned char* rowp = lds + slot * SLOT + row * ROWB;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) bf[kk] = lds_frag<T>(rowp, kk, g, row & (CH16 - 1));
   };
@@ -346,7 +364,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     }
   };
   // tile of u0 landed: the S-2 later tiles may still be in flight
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NJ));
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NLD));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -384,6 +402,8 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
         frag_t<T> bf[KSTEPS];
         load_b(slot, sub, bf);
         cur[sub] = score_subtile<T, DI, QPW>(f, bf);
+        if constexpr (kFp8)
+          cur[sub] *= *reinterpret_cast<const float*>(lds + slot * SLOT + TILEB + wave * 256 + 4 * (sub * 16 + c));
       }
     }
 #pragma unroll
@@ -396,7 +416,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     // loads; the S-2 tiles issued after it may still be in flight) before
     // any wave reads it, and every wave is done with slot `slot` before it
     // is refilled.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NJ));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NLD));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
@@ -425,7 +445,7 @@ __global__ __launch_bounds__(256) void scores_upper_fill_kernel(IndexerParams a,
 // B operands directly from the key cache.
 template <typename T, int DI, int NQ>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
-  constexpr int NT = 256, KSTEPS = DI / 32;
+  constexpr int NT = 256, KSTEPS = DI / kStepElems<T>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int b = blockIdx.z, t_first = blockIdx.y * NQ, s_begin = blockIdx.x * a.key_chunk;
   int q_pos0, n_kv;
@@ -451,11 +471,12 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
       const bool sv = s < n_kv;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk)
-        bf[kk] = sv ? load_frag<T>(kb + (size_t)s * DI + 32 * kk + 8 * g) : zero_frag<T>();
+        bf[kk] = sv ? load_frag<T>(kb + (size_t)s * DI + frag_off<T>(kk, g)) : zero_frag<T>();
     };
     auto emit = [&](int sub, const frag_t<T> (&bf)[KSTEPS]) {
-      const float e = score_subtile<T, DI, NQ>(f, bf);
+      float e = score_subtile<T, DI, NQ>(f, bf);
       const int s = s_begin + sub * 16 + c;
+      if constexpr (kStepElems<T> == 128) e *= a.kscale[(size_t)b * a.kv_cap + min(s, n_kv - 1)];
       if (t_mine < a.T) {
         if (s <= p_mine) __builtin_nontemporal_store(e, srow + s);
         else if (a.write_upper) __builtin_nontemporal_store(ninf, srow + s);
@@ -522,6 +543,7 @@ hipError_t launch_indexer_t(const IndexerParams& p, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_indexer(const IndexerParams& p, int dtype, int DI, hipStream_t st) {
+  if (dtype == kIndexerFp8) return DI == 128 && p.kscale ? launch_indexer_t<fp8e4m3, 128>(p, st) : hipErrorInvalidValue;
   if (dtype == 1) {
     if (DI == 128) return launch_indexer_t<bf16, 128>(p, st);
     if (DI == 64) return launch_indexer_t<bf16, 64>(p, st);

@@ -173,6 +173,35 @@ dsa_status dsa_forward_varlen(const dsa_dims* dims, const int32_t* seq_lens, con
                               int32_t* indices, uint32_t* mask, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* fp8 reading of the indexer (a precision study: the pages keep the
+ * indexer's tensors unquantised because top-k selection is sensitive to their
+ * precision [aiaulis para 5; aiu "What happened"; devotd section 3]).
+ *
+ * dsa_quantize_fp8 turns bf16 indexer rows (idx_dim 128) into e4m3 codes
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest value 448)
+ * with one float32 scale per row: scale = max|x| / 448 (1 for a zero row),
+ * code = e4m3(x / scale), division correctly rounded in float32, rounding to
+ * nearest with ties to the even mantissa.
+ *   queries: qidx [B][T][idx_heads][128] bf16, w [B][T][idx_heads] float32
+ *            -> qidx8 [B][T][idx_heads][128] codes, wq = w * scale [B][T][idx_heads]
+ *   keys:    rows q_pos0 .. q_pos0+T-1 of kidx [B][kv_capacity][128] bf16 (the
+ *            call's new tokens) -> the same rows of kidx8 [B][kv_capacity][128]
+ *            codes and kscale [B][kv_capacity] float32; other rows untouched.
+ * Pass NULL for all four query pointers or all three key pointers to skip
+ * that half (at least one half is required). dims->dtype must be DSA_BF16
+ * and idx_dim 128 (DSA_ERR_UNSUPPORTED otherwise).
+ *
+ * dsa_index_scores_fp8 is dsa_index_scores on the quantised tensors:
+ *   scores[b][i][s] = kscale[b][s] * sum_h wq[b][i][h] * max(0, sum_d qidx8[b][i][h][d] * kidx8[b][s][d])
+ * for s <= p (the products of codes summed in float32), -inf elsewhere; the
+ * scale factors come out of the ReLU because they are positive. Reads key
+ * rows and scales 0..n_kv-1. Same dims rules as the quantiser. */
+dsa_status dsa_quantize_fp8(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
+                            uint8_t* qidx8, float* wq, uint8_t* kidx8, float* kscale, void* stream);
+dsa_status dsa_index_scores_fp8(const dsa_dims* dims, const uint8_t* qidx8, const float* wq,
+                                const uint8_t* kidx8, const float* kscale, float* scores,
+                                void* stream);
+
 /* Problem sizes of the indexer front end (dsa_indexer_project). bf16 only.
  * Supported: hidden and q_rank multiples of 64; 1 <= idx_heads <= 32;
  * idx_dim in {32, 64, 128}; q_pos0 + n_q <= kv_capacity. */

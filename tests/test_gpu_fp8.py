@@ -1,0 +1,81 @@
+"""GPU parity of the fp8 indexer reading (dsa_quantize_fp8 and
+dsa_index_scores_fp8, through the C ABI) against the CPU oracle on the same
+seeded inputs: e4m3 codes, scales and folded weights bit for bit, scores
+within the float32 accumulation bound of the quantised operands, and the
+top-k selection on those scores (exact up to near-ties)."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_lightning_indexer_03_amd as dsa
+from dsa_workloads import Workload, make_inputs
+from oracle import round_scores_fp32, select_topk
+from oracle.fp8_indexer import index_scores_fp8, quantize_rows_fp8
+from tests.dsa_check import score_bound, selection_ok, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    print(f"\n[gpu-test] {request.node.nodeid}", flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def _codes(t):
+    """uint8 e4m3 codes -> float64 values."""
+    return t.cpu().view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+CASES = [
+    # name, B, T, q_pos0, n_kv, cap, HI, top_k, integer
+    ("prefill_T512", 1, 512, 0, 512, 512, 32, 100, False),
+    ("ragged_batch", 2, 100, 37, 150, 160, 20, 40, False),
+    ("multi_tile_chunk", 1, 200, 700, 900, 900, 32, 300, False),
+    ("decode_single", 4, 1, 2999, 3000, 3000, 32, 333, False),
+    ("decode_multi_query", 2, 5, 495, 500, 512, 16, 64, False),
+    ("integer_inputs", 1, 300, 0, 300, 300, 32, 40, True),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fp8_indexer_parity(case):
+    name, B, T, p0, nkv, cap, HI, k, integer = case
+    full = Workload(name=name, dtype="bf16", batch=B, n_q=p0 + T, q_pos0=0, n_kv=nkv, idx_heads=HI, idx_dim=128,
+                    top_k=k, heads=4, kv_heads=4, head_dim=64, seed=zlib.crc32(name.encode()) % 1000,
+                    integer_indexer=integer, qidx_std=1 / math.sqrt(128), kidx_std=1.0, w_std=1 / math.sqrt(HI))
+    cpu = make_inputs(full, "cpu", kv_capacity=cap)
+    qidx, w, kidx = cpu["qidx"][:, p0:].contiguous(), cpu["w"][:, p0:].contiguous(), cpu["kidx"]
+    g_q, g_w, g_k = qidx.to(DEV), w.to(DEV), kidx.to(DEV)
+    q8, wq = dsa.quantize_fp8(g_q, g_w)
+    k8, ks = dsa.quantize_keys_fp8(g_k, pos0=0, count=nkv)
+    sc = dsa.index_scores_fp8(q8, wq, k8, ks, q_pos0=p0, n_kv=nkv)
+    mask, idx = dsa.topk_mask(sc, q_pos0=p0, n_kv=nkv, top_k=k)
+    torch.cuda.synchronize()
+    sc_np, idx_np = to_np(sc), to_np(idx)
+    q8_np, k8_np = _codes(q8), _codes(k8)
+    for b in range(B):
+        s64, oq8, owq, ok8, oks = index_scores_fp8(to_np(qidx[b]).astype(np.float64),
+                                                   to_np(w[b]), to_np(kidx[b, :nkv]).astype(np.float64), p0)
+        # quantisation: bit-exact codes, scales and folded weights
+        assert np.array_equal(q8_np[b], oq8)
+        assert np.array_equal(k8_np[b, :nkv], ok8)
+        assert np.array_equal(to_np(ks[b, :nkv]), oks)
+        assert np.array_equal(to_np(wq[b]), owq)
+        s32 = round_scores_fp32(s64)
+        for i in range(T):
+            p = p0 + i
+            bound = oks[: p + 1].astype(np.float64) * score_bound(oq8[i], owq[i].astype(np.float64),
+                                                                  ok8[: p + 1], 128, HI)
+            err = np.abs(sc_np[b, i, : p + 1].astype(np.float64) - s64[i, : p + 1])
+            assert np.all(err <= bound), f"b{b} row {i}: fp8 score error {err.max()} above bound"
+            assert np.all(np.isneginf(sc_np[b, i, p + 1 :]))
+            gsel = np.array(sorted(int(x) for x in idx_np[b, i] if x >= 0))
+            osel = select_topk(s32[i], p, k)
+            ok, nd, _ = selection_ok(gsel, osel, s64[i], p, k)
+            assert ok, f"b{b} row {i}: selection differs beyond near-ties ({nd})"
