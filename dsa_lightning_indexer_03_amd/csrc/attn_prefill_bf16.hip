@@ -12,12 +12,15 @@
 // fragment a wave reads from LDS is used for both of its query blocks (512 B
 // of LDS reads per key per wave against 32 * 512 flops of matrix work). At
 // at most 256 registers per lane one workgroup fills a CU, two waves per
-// SIMD, so one wave's softmax overlaps the other's matrix work; its 256
-// queries share each tile loaded into LDS (LDS bandwidth, shared by those
-// loads and the fragment reads, is what limits this kernel). (Waves of 64
-// queries halve the LDS traffic but need more than 256 registers: their
-// accumulators then live in AGPRs, which the compiler copies around every
-// tile, and they measured slower.)
+// SIMD, so one wave's softmax can overlap the other's matrix work; its 256
+// queries share each tile loaded into LDS. With the operand reads free of
+// bank conflicts LDS is about half busy; the exp2 and masking work of the
+// softmax (VALU, exp2 at quarter rate) and the matrix work of the two waves
+// on a SIMD overlap only partly, and that is what bounds the kernel. (Waves
+// of 64 queries halve the LDS traffic but need more than 256 registers:
+// their accumulators then live in AGPRs, which the compiler copies around
+// every tile, and they measured slower; waves of 16 queries, four per SIMD,
+// measured slower too.)
 //
 // Matrix layout (v_mfma_f32_16x16x32_bf16, see dsa_device.hpp):
 //   S^T = K Q^T   A = K rows from LDS, B = Q^T; lane (c, g) ends up holding

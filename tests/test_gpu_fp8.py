@@ -79,3 +79,30 @@ def test_fp8_indexer_parity(case):
             osel = select_topk(s32[i], p, k)
             ok, nd, _ = selection_ok(gsel, osel, s64[i], p, k)
             assert ok, f"b{b} row {i}: selection differs beyond near-ties ({nd})"
+
+
+def test_fp8_indexer_prefill_L4096_sampled_rows():
+    """Full-size prefill workload (the shape the bench's fp8 study runs): all
+    rows scored and selected on the GPU, sampled rows checked against the
+    oracle."""
+    from dsa_workloads import WORKLOADS, sample_rows
+    wl = WORKLOADS["prefill_bf16_L4096"]
+    cpu = make_inputs(wl, "cpu")
+    g_q, g_w, g_k = cpu["qidx"].to(DEV), cpu["w"].to(DEV), cpu["kidx"].to(DEV)
+    q8, wq = dsa.quantize_fp8(g_q, g_w)
+    k8, ks = dsa.quantize_keys_fp8(g_k)
+    sc = dsa.index_scores_fp8(q8, wq, k8, ks, q_pos0=0, n_kv=wl.n_kv)
+    _, idx = dsa.topk_mask(sc, q_pos0=0, n_kv=wl.n_kv, top_k=wl.top_k)
+    torch.cuda.synchronize()
+    sc_np, idx_np = to_np(sc[0]), to_np(idx[0])
+    q64, w32, k64 = to_np(cpu["qidx"][0]).astype(np.float64), to_np(cpu["w"][0]), to_np(cpu["kidx"][0]).astype(np.float64)
+    assert np.array_equal(_codes(k8[0]), quantize_rows_fp8(k64)[0])
+    for i in sample_rows(wl, 48, seed=7):
+        s64, oq8, owq, ok8, oks = index_scores_fp8(q64[i : i + 1], w32[i : i + 1], k64, i)
+        bound = oks[: i + 1].astype(np.float64) * score_bound(oq8[0], owq[0].astype(np.float64), ok8[: i + 1],
+                                                                128, wl.idx_heads)
+        err = np.abs(sc_np[i, : i + 1].astype(np.float64) - s64[0, : i + 1])
+        assert np.all(err <= bound), f"row {i}: fp8 score error {err.max()} above bound"
+        gsel = np.array(sorted(int(x) for x in idx_np[i] if x >= 0))
+        ok, nd, _ = selection_ok(gsel, select_topk(round_scores_fp32(s64)[0], i, wl.top_k), s64[0], i, wl.top_k)
+        assert ok, f"row {i}: selection differs beyond near-ties ({nd})"
