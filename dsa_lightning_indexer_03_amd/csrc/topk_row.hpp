@@ -13,7 +13,8 @@
 // [w*EPT*64, (w+1)*EPT*64), element e of lane l is token w*EPT*64 + e*64 + l,
 // so a wave ballot over element e is exactly one 64-bit mask word. A radix
 // select (11 + 11 + 10 bits, LDS histograms) finds the key of the k-th
-// largest score and how many of the tokens equal to it are kept; when only
+// largest score (or only its leading digits, once the bin holding it is
+// kept whole) and how many of the tokens equal to it are kept; when only
 // some of the equal tokens are kept, their ranks in index order come from
 // ballots, a per-wave prefix and a workgroup scan. The row is read from HBM
 // once.
@@ -110,6 +111,7 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
   uint32_t prefix = 0;
   uint32_t rem = (uint32_t)a.top_k;  // rank of the threshold within the current candidates
   uint32_t count_eq = 0;
+  int thr_shift = 0;  // the threshold is a prefix: keys compare as key >> thr_shift
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -150,16 +152,23 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
     count_eq = found[2];
     prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
     __syncthreads();
+    // Every token of the threshold's bin is kept: the prefix already
+    // separates kept from dropped tokens, and the later digits need not be
+    // resolved (the usual case after 22 bits on continuous scores).
+    if (pass < 2 && rem == count_eq) {
+      thr_shift = shift;
+      break;
+    }
   }
   const uint32_t thr = prefix;
-  const bool all_eq = rem == count_eq;  // every token equal to the threshold is kept
+  const bool all_eq = rem == count_eq;  // every token equal to the threshold (prefix) is kept
 
   // Index-order rank base of this wave's threshold-equal tokens.
   uint32_t eq_base = 0;
   if (!all_eq) {
     uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) cnt += __popcll(ballot64(key(e) == thr));
+    for (int e = 0; e < EPT; ++e) cnt += __popcll(ballot64((key(e) >> thr_shift) == thr));
     if (lane == 0) red[wave] = cnt;
     __syncthreads();
     for (int w = 0; w < wave; ++w) eq_base += red[w];
@@ -171,8 +180,10 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
   const uint64_t lt = lanemask_lt();
   auto select = [&](int e, uint32_t& running_eq) -> bool {
     const uint32_t k = key(e);
-    const bool eq = k == thr;  // thr is a finite key, never the 0 sentinel
-    bool s = k > thr;
+    // thr is a finite key's prefix: never that of the 0 sentinel, whose every
+    // prefix is 0 (finite keys are at least 0x00800000)
+    const bool eq = (k >> thr_shift) == thr;
+    bool s = (k >> thr_shift) > thr;
     if (all_eq) return s || eq;
     const uint64_t be = ballot64(eq);
     s = s || (eq && running_eq + (uint32_t)__popcll(be & lt) < rem);
