@@ -197,3 +197,20 @@ def test_indexer_project_pointers_and_workspace():
     # a 4096-token prefill needs partials only for the thin k / projection product
     big = _pdims(n_q=4096, kv_capacity=4096, hidden=7168, q_rank=1536)
     assert dsa.proj_workspace_size(big) == 8 * 4096 * 160 * 4
+
+
+def test_fp8_entry_points_validation():
+    lib = dsa.lib()
+    q = lambda d, *p: lib.dsa_quantize_fp8(ctypes.byref(d), *p, None)
+    s = lambda d, *p: lib.dsa_index_scores_fp8(ctypes.byref(d), *p, None)
+    # fp8 needs bf16 inputs with idx_dim 128
+    assert q(_dims(idx_dim=64), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == ERR_UNSUPPORTED
+    assert q(_dims(dtype=dsa.DSA_FP32, idx_dim=64), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == ERR_UNSUPPORTED
+    assert s(_dims(idx_dim=32), FAKE, FAKE, FAKE, FAKE, FAKE) == ERR_UNSUPPORTED
+    # nothing to quantise, or half a group given
+    assert q(_dims(), None, None, None, None, None, None, None) == ERR_NULL
+    assert q(_dims(), FAKE, FAKE, None, None, FAKE, None, None) == ERR_NULL       # qidx8 missing
+    assert q(_dims(), None, None, FAKE, None, None, FAKE, None) == ERR_NULL       # kscale missing
+    assert q(_dims(), FAKE, FAKE + 4, None, FAKE, FAKE, None, None) == ERR_MISALIGNED
+    assert s(_dims(), FAKE, FAKE, FAKE, None, FAKE) == ERR_NULL                   # kscale missing
+    assert s(_dims(q_pos0=60), FAKE, FAKE, FAKE, FAKE, FAKE) == ERR_SHAPE
