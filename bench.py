@@ -51,12 +51,18 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The GPU reaches its steady clocks only after tens of milliseconds of
+    # back-to-back work: a 6 ms timed region after a 1.5 ms warmup measured
+    # this step 17% slower than the steady state. The defaults time about
+    # 50 ms of headline steps after about 25 ms of warmup.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--secondary", default=",".join(SECONDARY),
                     help="comma-separated workloads also measured ('' for none)")
-    ap.add_argument("--secondary-steps", type=int, default=5)
+    ap.add_argument("--secondary-steps", type=int, default=0,
+                    help="steps timed per secondary workload (0 = enough for about 100 ms, "
+                         "at least 3, after as many warmup steps)")
     ap.add_argument("--fp8-study", default=f"{HEADLINE},longctx_bf16_L65536_chunk4096",
                     help="workloads on which the fp8 indexer reading is timed and its selection "
                          "compared with bf16 ('' for none)")
@@ -235,6 +241,14 @@ def run_gpu(wl, steps, warmup, torch, dsa, make_inputs):
         "dominant": dominant,
         "calls_per_step": len(calls),
     }
+
+
+def secondary_steps_for(wl):
+    """Steps (and as many warmup steps) that fill about 100 ms for a
+    secondary workload, from its algorithmic work at a nominal rate:
+    chunked long-context steps take tens of ms, a decode step half of one."""
+    est_ms = 25.0 if wl.chunks > 1 else 0.5
+    return int(min(200, max(3, round(100.0 / est_ms))))
 
 
 def front_end_work(fw):
@@ -416,11 +430,12 @@ def main():
     log(f"[bench] {wl.name}: {head['ms_per_step']:.3f} ms/step, {head['value']:.4g} queries/s")
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
-        r = run_gpu(WORKLOADS[name], args.secondary_steps, min(args.warmup, 2), torch, dsa, make_inputs)
+        steps2 = args.secondary_steps or secondary_steps_for(WORKLOADS[name])
+        r = run_gpu(WORKLOADS[name], steps2, steps2, torch, dsa, make_inputs)
         log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step, {r['value']:.4g} queries/s")
         secondary.append({
             "workload": name, "value": r["value"], "unit": "queries/s",
-            "ms_per_step": round(r["ms_per_step"], 4), "steps": args.secondary_steps,
+            "ms_per_step": round(r["ms_per_step"], 4), "steps": steps2, "warmup": steps2,
             "roofline": _roofline(r["dominant"], name), "kernels": r["kernels"],
         })
     front_end = []
