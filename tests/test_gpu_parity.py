@@ -198,6 +198,8 @@ EDGE = [
     ("mqa_prefill_ragged", "bf16", 2, 130, 37, 167, 170, 32, 128, 50, 32, 1, 128, False),
     ("mqa_prefill_multi_tile", "bf16", 1, 200, 500, 700, 700, 32, 128, 300, 32, 1, 128, False),
     ("mqa_prefill_h16_ties", "bf16", 1, 300, 0, 300, 300, 32, 128, 40, 16, 1, 128, True),
+    # one K/V row per token at decode shape: the gather path with a single KV head
+    ("mqa_decode", "bf16", 3, 2, 2998, 3000, 3000, 32, 128, 500, 32, 1, 128, False),
 ]
 
 
