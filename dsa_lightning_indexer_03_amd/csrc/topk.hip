@@ -16,11 +16,325 @@ __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
   topk_select_row<NW, EPT_R, EPT_L>(a, blockIdx.x, blockIdx.y, sh);
 }
 
+
+// Long rows (prefill chunks deep into a long cache): one 4-wave workgroup
+// per row, four rows per CU (33 KiB of LDS and at most 128 registers each),
+// the row streamed from memory, two 4096-token blocks ahead, instead of held
+// on chip.
+//
+//  1. A threshold is guessed from a sample of the row (64-token segments
+//     0, 8, 16, ...): the 22-bit key prefix of the sample's
+//     (1.25 k ns / n + 16)-th largest score, so that about 1.25 k + 128 of
+//     the row's scores reach it.
+//  2. One pass over the row compacts every token whose key prefix reaches
+//     the guess into LDS, in index order (at most kLongCap tokens).
+//  3. When between k and kLongCap tokens survived, the k-th largest score of
+//     the row is the k-th largest survivor (every other score is below the
+//     guess), so a radix select over the survivors, ties to the lower index,
+//     gives the row's selection exactly. The mask is assembled in LDS.
+//  4. Otherwise (an unrepresentative sample, or heavy ties) the workgroup
+//     finds the exact threshold by radix passes that re-read the row, and a
+//     last pass writes the selection: slower, exact.
+constexpr int kLongNW = 4, kLongNT = kLongNW * 64;
+constexpr int kLongCap = 4096;               // survivors held in LDS
+constexpr int kLongEPT = 16;                 // row elements per thread per block
+constexpr int kLongBlock = kLongNT * kLongEPT;  // 4096 tokens per block
+constexpr int kLongSampleEPT = kTopkMaxRow / 8 / kLongNT;  // sample elements per thread (32)
+
+struct TopkLongShared {
+  uint32_t key[kLongCap];
+  uint16_t idx[kLongCap];  // token indices (rows hold at most 65536 tokens)
+  uint32_t hist[2048];   // radix histograms, then the mask bitmap (<= 2048 words)
+  uint32_t wcnt[2][64];  // per (element, wave) counts of one block, double-buffered
+  uint32_t red[kLongNW];
+  uint32_t found[3];
+};
+
+// Exclusive position of this lane's flagged element e in (e, wave, lane)
+// order, for kLongEPT elements per thread; returns the block total. wc is a
+// 64-entry LDS array; one barrier inside.
+__device__ __forceinline__ uint32_t ordered_positions(const uint64_t (&bal)[kLongEPT], uint32_t (&pos)[kLongEPT],
+                                                      uint32_t* wc) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  static_assert(kLongEPT * kLongNW == 64, "one count per lane");
+  if (lane < kLongEPT) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int e = 0; e < kLongEPT; ++e)
+      if (lane == e) mine = (uint32_t)__popcll(bal[e]);
+    wc[lane * kLongNW + wave] = mine;
+  }
+  __syncthreads();
+  const uint32_t v = wc[lane];
+  const uint32_t incl = wave_inclusive_sum(v);
+  const uint32_t excl = incl - v;
+  const uint64_t lt = lanemask_lt();
+#pragma unroll
+  for (int e = 0; e < kLongEPT; ++e)
+    pos[e] = (uint32_t)__shfl((int)excl, e * kLongNW + wave, 64) + (uint32_t)__popcll(bal[e] & lt);
+  return (uint32_t)__shfl((int)incl, 63, 64);
+}
+
+// Radix select of rank `rank` (1 = largest) over the keys that for_each
+// visits: for_each(f) calls f(key) for every candidate key of this thread
+// (key 0 = no token, never counted). Returns the threshold as (thr, shift):
+// the tokens kept are key >> shift > thr, plus, among key >> shift == thr,
+// all of them when all_eq, else the first `rem` in index order.
+template <typename ForEach>
+__device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t rank, TopkLongShared& sh,
+                                                  uint32_t& thr, int& shift_out, uint32_t& rem, bool& all_eq) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, count_eq = 0;
+  rem = rank;
+  int thr_shift = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nbins = pass == 2 ? 1024 : 2048;
+    const int pshift = pass == 0 ? 32 : (pass == 1 ? 21 : 10);
+    for (int i = tid; i < nbins; i += kLongNT) sh.hist[i] = 0;
+    __syncthreads();
+    for_each([&](uint32_t k) {
+      const bool cand = k != 0u && (pass == 0 || (k >> pshift) == prefix);
+      if (cand) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
+    });
+    __syncthreads();
+    const int bpt = nbins / kLongNT;
+    const int top = nbins - tid * bpt;
+    uint32_t local = 0;
+    for (int d = top - 1; d >= top - bpt; --d) local += sh.hist[d];
+    const uint32_t incl = block_inclusive_sum<kLongNW>(local, sh.red);
+    uint32_t cum = incl - local;
+    if (cum < rem && rem <= incl) {
+      for (int d = top - 1; d >= top - bpt; --d) {
+        const uint32_t h = sh.hist[d];
+        if (cum < rem && rem <= cum + h) {
+          sh.found[0] = (uint32_t)d;
+          sh.found[1] = cum;
+          sh.found[2] = h;
+          break;
+        }
+        cum += h;
+      }
+    }
+    __syncthreads();
+    const uint32_t d = sh.found[0];
+    rem -= sh.found[1];
+    count_eq = sh.found[2];
+    prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
+    __syncthreads();
+    thr_shift = shift;
+    if (rem == count_eq) break;  // the threshold's bin is kept whole
+  }
+  thr = prefix;
+  shift_out = thr_shift;
+  all_eq = rem == count_eq;
+}
+
+__global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) void topk_long_kernel(TopkParams a) {
+  __shared__ TopkLongShared sh;
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int q_pos0, n_kv;
+  seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
+  const int p = q_pos0 + t, n = p + 1;
+  const size_t row = (size_t)b * a.T + t;
+  const int nwords = a.Lpad / 32;
+  const float* srow = a.scores + row * a.Lpad;
+  uint32_t* mrow = a.mask + row * nwords;
+  int32_t* irow = a.indices ? a.indices + row * a.top_k : nullptr;
+  const uint32_t k = (uint32_t)a.top_k;
+
+  if (a.top_k >= n) {  // every candidate is kept
+    for (int wi = tid; wi < nwords; wi += kLongNT) {
+      const int lo = wi * 32;
+      mrow[wi] = lo + 32 <= n ? 0xffffffffu : (lo < n ? (1u << (n - lo)) - 1u : 0u);
+    }
+    if (irow)
+      for (int j = tid; j < a.top_k; j += kLongNT) irow[j] = j < n ? j : -1;
+    return;
+  }
+  const int nblocks = (n + kLongBlock - 1) / kLongBlock;
+  // element e of this thread in block blk is token blk * kLongBlock + e * kLongNT + tid
+  auto load_block = [&](int blk, float (&v)[kLongEPT]) {
+#pragma unroll
+    for (int e = 0; e < kLongEPT; ++e) v[e] = srow[min(blk * kLongBlock + e * kLongNT + tid, n - 1)];
+  };
+  auto block_key = [&](int blk, int e, float v) -> uint32_t {
+    return blk * kLongBlock + e * kLongNT + tid < n ? orderable_key(v) : 0u;
+  };
+
+  // 1. Threshold guess from the sample (or none: every token survives).
+  uint32_t guess = 0;  // survivors: key >> 10 >= guess (and a token)
+  if (n > kLongCap) {
+    const int nseg = (n + 63) / 64;
+    const int ns = ((nseg + 7) / 8) * 64;  // sample slots (the last segment may be partial)
+    uint32_t skey[kLongSampleEPT];
+    {
+      float v[kLongSampleEPT];
+#pragma unroll
+      for (int e = 0; e < kLongSampleEPT; ++e) {
+        const int u = e * kLongNT + tid;
+        v[e] = srow[min(512 * (u >> 6) + (u & 63), n - 1)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < kLongSampleEPT; ++e) {
+        const int u = e * kLongNT + tid, s = 512 * (u >> 6) + (u & 63);
+        skey[e] = u < ns && s < n ? orderable_key(v[e]) : 0u;
+      }
+    }
+    const uint32_t nsv = (uint32_t)(64 * (n / 512) + min(n % 512, 64));  // tokens in the sample
+    const uint32_t ks = min(nsv, (uint32_t)((1.25f * (float)k * (float)nsv) / (float)n) + 16u);
+    uint32_t thr, rem;
+    int shift;
+    bool all_eq;
+    long_radix_select([&](auto f) {
+#pragma unroll
+      for (int e = 0; e < kLongSampleEPT; ++e) f(skey[e]);
+    }, ks, sh, thr, shift, rem, all_eq);
+    // the survivor test is on 22-bit prefixes: widen a shorter one
+    guess = shift >= 10 ? thr << (shift - 10) : thr >> (10 - shift);
+  }
+
+  // 2. Survivors, in index order, into LDS.
+  uint32_t total = 0;
+  {
+    float cur[kLongEPT], nxt[kLongEPT], nxt2[kLongEPT];
+    load_block(0, cur);
+    if (nblocks > 1) load_block(1, nxt);
+    for (int blk = 0; blk < nblocks; ++blk) {
+      if (blk + 2 < nblocks) load_block(blk + 2, nxt2);
+      uint64_t bal[kLongEPT];
+      uint32_t keys[kLongEPT], pos[kLongEPT];
+#pragma unroll
+      for (int e = 0; e < kLongEPT; ++e) {
+        keys[e] = block_key(blk, e, cur[e]);
+        bal[e] = ballot64(keys[e] != 0u && (keys[e] >> 10) >= guess);
+      }
+      const uint32_t cnt = ordered_positions(bal, pos, sh.wcnt[blk & 1]);
+#pragma unroll
+      for (int e = 0; e < kLongEPT; ++e) {
+        const uint32_t at = total + pos[e];
+        if (((bal[e] >> lane) & 1ull) && at < (uint32_t)kLongCap) {
+          sh.key[at] = keys[e];
+          sh.idx[at] = (uint16_t)(blk * kLongBlock + e * kLongNT + tid);
+        }
+      }
+      total += cnt;
+#pragma unroll
+      for (int e = 0; e < kLongEPT; ++e) {
+        cur[e] = nxt[e];
+        nxt[e] = nxt2[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  if (total >= k && total <= (uint32_t)kLongCap) {
+    // 3. Exact selection among the survivors (index order = LDS order).
+    constexpr int CE = kLongCap / kLongNT;  // survivor slots per thread (16)
+    static_assert(CE == kLongEPT, "survivor slots use the block layout");
+    uint32_t thr, rem;
+    int shift;
+    bool all_eq;
+    long_radix_select([&](auto f) {
+#pragma unroll
+      for (int e = 0; e < CE; ++e) {
+        const uint32_t u = (uint32_t)(e * kLongNT + tid);
+        f(u < total ? sh.key[u] : 0u);
+      }
+    }, k, sh, thr, shift, rem, all_eq);
+    // tie ranks among threshold-equal survivors, then the kept flags
+    uint64_t beq[kLongEPT], bsel[kLongEPT];
+    uint32_t ckey[kLongEPT], pos[kLongEPT];
+#pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      const uint32_t u = (uint32_t)(e * kLongNT + tid);
+      ckey[e] = u < total ? sh.key[u] : 0u;
+      beq[e] = ballot64(ckey[e] != 0u && (ckey[e] >> shift) == thr);
+    }
+    ordered_positions(beq, pos, sh.wcnt[0]);
+#pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      const bool eq = (beq[e] >> lane) & 1ull;
+      const bool gt = ckey[e] != 0u && (ckey[e] >> shift) > thr;
+      bsel[e] = ballot64(gt || (eq && (all_eq || pos[e] < rem)));
+    }
+    for (int i = tid; i < nwords; i += kLongNT) sh.hist[i] = 0;  // bitmap
+    const uint32_t nsel = ordered_positions(bsel, pos, sh.wcnt[1]);
+    (void)nsel;
+#pragma unroll
+    for (int e = 0; e < CE; ++e) {
+      if ((bsel[e] >> lane) & 1ull) {
+        const int s = sh.idx[e * kLongNT + tid];
+        atomicOr(&sh.hist[s >> 5], 1u << (s & 31));
+        if (irow && pos[e] < k) irow[pos[e]] = s;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nwords; i += kLongNT) mrow[i] = sh.hist[i];
+    return;
+  }
+
+  // 4. Exact threshold by passes over the row, then the selection.
+  uint32_t thr, rem;
+  int shift;
+  bool all_eq;
+  long_radix_select([&](auto f) {
+    for (int blk = 0; blk < nblocks; ++blk) {
+      float v[kLongEPT];
+      load_block(blk, v);
+#pragma unroll
+      for (int e = 0; e < kLongEPT; ++e) f(block_key(blk, e, v[e]));
+    }
+  }, k, sh, thr, shift, rem, all_eq);
+  uint32_t eq_before = 0, sel_before = 0;
+  for (int blk = 0; blk < nblocks; ++blk) {
+    float v[kLongEPT];
+    load_block(blk, v);
+    uint64_t beq[kLongEPT], bsel[kLongEPT];
+    uint32_t keys[kLongEPT], pos[kLongEPT];
+#pragma unroll
+    for (int e = 0; e < kLongEPT; ++e) {
+      keys[e] = block_key(blk, e, v[e]);
+      beq[e] = ballot64(keys[e] != 0u && (keys[e] >> shift) == thr);
+    }
+    const uint32_t neq = ordered_positions(beq, pos, sh.wcnt[0]);
+#pragma unroll
+    for (int e = 0; e < kLongEPT; ++e) {
+      const bool eq = (beq[e] >> lane) & 1ull;
+      const bool gt = keys[e] != 0u && (keys[e] >> shift) > thr;
+      bsel[e] = ballot64(gt || (eq && (all_eq || eq_before + pos[e] < rem)));
+    }
+    const uint32_t nsel = ordered_positions(bsel, pos, sh.wcnt[1]);
+#pragma unroll
+    for (int e = 0; e < kLongEPT; ++e) {
+      // the ballot of element e in wave w is mask word pair (blk * kLongBlock + e * kLongNT + 64 w) / 64
+      const int s0 = blk * kLongBlock + e * kLongNT + 64 * wave;
+      if (lane == 0 && s0 / 32 < nwords)
+        *reinterpret_cast<uint2*>(mrow + s0 / 32) = make_uint2((uint32_t)bsel[e], (uint32_t)(bsel[e] >> 32));
+      if (irow && ((bsel[e] >> lane) & 1ull) && sel_before + pos[e] < k) irow[sel_before + pos[e]] = s0 + lane;
+    }
+    eq_before += neq;
+    sel_before += nsel;
+    __syncthreads();  // wcnt reuse
+  }
+  for (int wp = nblocks * (kLongBlock / 64) + tid; 2 * wp < nwords; wp += kLongNT)
+    *reinterpret_cast<uint2*>(mrow + 2 * wp) = make_uint2(0u, 0u);
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   const int nmax = p.q_pos0 + p.T;  // longest candidate row in the call
   dim3 grid(p.T, p.B);
+  // Many long rows: stream each row through a small workgroup (several rows
+  // per CU) with a sampled threshold; its survivors fit the LDS for top_k up
+  // to 2048.
+  if (nmax > 16384 && nmax <= kTopkMaxRow && p.top_k <= 2048 && (long long)p.B * p.T >= 512) {
+    hipLaunchKernelGGL(topk_long_kernel, grid, dim3(kLongNT), 0, st, p);
+    return hipGetLastError();
+  }
   // Rows are latency-bound chains of barriers and LDS histograms, so the
   // smallest workgroup that holds a row (keys in registers) wins: more rows
   // are then in flight per CU.

@@ -258,6 +258,83 @@ def test_topk_kernel_on_crafted_scores(n_kv, T, top_k):
         assert np.array_equal(mask[i], pack_mask(sel, n_kv)), f"row {i} mask"
 
 
+LONG_TOPK = [
+    # name, T, n_kv, top_k, score recipe; every call has > 16384 candidates in
+    # its longest row and >= 512 rows, the shape of the streamed long-row top-k
+    ("random", 600, 40000, 2048, "normal"),
+    ("random_k100", 520, 65536, 100, "normal"),
+    # the sampled segments (64-token segments 0, 8, 16, ...) hold the best
+    # scores, so the sampled threshold keeps too few tokens: exact fallback
+    ("sample_misses", 520, 30000, 2048, "boost_sampled"),
+    # one value everywhere (and +-0): every token survives the guess (overflow)
+    ("all_equal", 512, 20000, 2048, "constant"),
+    # few distinct values: huge tie groups at the threshold
+    ("integer_ties", 512, 24000, 2048, "integers"),
+    # rows from 1 to 16800 candidates in one call: keep-all rows, rows short
+    # enough to skip the sample, sampled rows
+    ("mixed_lengths", 16800, 16800, 2048, "normal"),
+]
+
+
+def _long_topk_scores(recipe, T, L, q_pos0, seed):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    if recipe == "constant":
+        s = torch.full((1, T, L), 1.5, device=DEV)
+        s[:, :, ::5] = 0.0
+        s[:, :, 1::5] = -0.0
+        s[:, :, 2::5] = 0.0
+        s[:, :, 3::5] = 1.5
+        s[:, :, 4::5] = 1.5
+        return s
+    if recipe == "integers":
+        return torch.randint(-3, 4, (1, T, L), device=DEV, generator=gen).float()
+    s = torch.randn((1, T, L), device=DEV, generator=gen)
+    if recipe == "boost_sampled":
+        tok = torch.arange(L, device=DEV)
+        s[:, :, (tok // 64) % 8 == 0] += 10.0
+    return s
+
+
+@pytest.mark.parametrize("case", LONG_TOPK, ids=[c[0] for c in LONG_TOPK])
+def test_topk_long_rows_streamed(case):
+    """The streamed long-row top-k (sampled threshold, survivors compacted in
+    LDS, exact re-reading fallback): masks and index lists bit-exact against
+    the oracle's selection on the same float32 scores; on the mixed-length
+    call, every row's kept count and mask extent, and sampled rows exactly."""
+    name, T, n_kv, top_k, recipe = case
+    q_pos0 = n_kv - T
+    L = dsa.lpad(n_kv)
+    scores = _long_topk_scores(recipe, T, L, q_pos0, zlib.crc32(name.encode()))
+    mask, idx = dsa.topk_mask(scores, q_pos0=q_pos0, n_kv=n_kv, top_k=top_k)
+    torch.cuda.synchronize()
+    if T > 2000:
+        # kept counts on every row: min(p + 1, top_k), no bit past p
+        pc = torch.zeros(T, dtype=torch.int64, device=DEV)
+        m = mask[0].to(torch.int64) & 0xFFFFFFFF
+        for bit in range(32):
+            pc += ((m >> bit) & 1).sum(dim=1)
+        want = torch.clamp(torch.arange(T, device=DEV) + q_pos0 + 1, max=top_k)
+        assert torch.equal(pc, want)
+        last = (idx[0].max(dim=1).values).to(torch.int64)
+        assert torch.all(last <= torch.arange(T, device=DEV) + q_pos0)
+        rows = sorted({0, 1, top_k - 2, top_k - 1, top_k, 4095, 4096, 4097, 8191, 8192, T - 1}
+                      | set(np.random.default_rng(1).choice(T, 120, replace=False).tolist()))
+    else:
+        rows = range(T)
+    rsel = torch.as_tensor(list(rows), device=DEV)
+    s_h = to_np(scores[0, rsel])
+    m_h = to_np(mask[0, rsel]).view(np.uint32)
+    i_h = to_np(idx[0, rsel])
+    for j, i in enumerate(rows):
+        p = q_pos0 + i
+        sel = select_topk(round_scores_fp32(s_h[j]), p, top_k)
+        want = np.full(top_k, -1, dtype=np.int32)
+        want[: len(sel)] = sel
+        assert np.array_equal(i_h[j], want), f"{name} row {i}"
+        assert np.array_equal(m_h[j], pack_mask(sel, n_kv)), f"{name} row {i} mask"
+
+
 @pytest.mark.parametrize("T,q_pos0,n_kv,H,Hkv,D,dt", [(130, 20, 200, 4, 2, 128, "bf16"),
                                                       (1, 700, 701, 8, 8, 64, "bf16"),
                                                       (6, 300, 306, 16, 4, 128, "bf16"),
