@@ -415,6 +415,11 @@ VARLEN = [
     ("varlen_gqa_multi_query", "bf16", 3, 3000, [3, 2999, 1500, 700], 32, 128, 333, 16, 4, 64, False),
     ("varlen_integer_ties", "bf16", 1, 3000, [3000, 2500, 64, 65], 32, 128, 40, 32, 32, 128, True),
     ("varlen_fp32", "fp32", 2, 900, [900, 2, 400], 4, 32, 64, 4, 4, 64, False),
+    # 512 query rows, longest cache above 16384 tokens: the streamed long-row
+    # top-k with per-sequence extents (keep-all, unsampled and sampled rows)
+    ("varlen_many_long_rows", "bf16", 8, 17000,
+     [17000, 8, 1000, 1001, 1007, 4096, 4104, 16385] + [int(x) for x in np.random.default_rng(7).integers(8, 17001, 56)],
+     4, 32, 1000, 4, 4, 64, False),
 ]
 
 
