@@ -66,6 +66,9 @@ def parse():
     ap.add_argument("--fp8-study", default=f"{HEADLINE},longctx_bf16_L65536_chunk4096",
                     help="workloads on which the fp8 indexer reading is timed and its selection "
                          "compared with bf16 ('' for none)")
+    ap.add_argument("--stream-study", default="longctx_mqa_bf16_L65536_chunk4096",
+                    help="workloads on which the streamed selection (dsa_forward_stream_select) is timed "
+                         "beside the materialised one ('' for none)")
     ap.add_argument("--front-end-steps", type=int, default=20,
                     help="calls timed per indexer front-end workload (0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -368,6 +371,48 @@ def fp8_indexer_study(wl, reps, torch, dsa, make_inputs):
 
 # ----------------------------------------------------------------------------- CPU oracle timing
 
+def stream_select_study(wl, reps, torch, dsa, make_inputs):
+    """Whole-layer steps with the selection streamed (sampled scores, survivor
+    lists) against the default materialised one, on the same inputs: time per
+    step of each and whether every index list came out identical."""
+    dev = torch.device("cuda:0")
+    g = make_inputs(wl, dev)
+    calls = chunk_calls(wl)
+    B = wl.batch
+    big = calls[-1]
+    dims = dsa.make_dims(batch=B, n_q=big[1], q_pos0=big[0], n_kv=big[2], kv_capacity=g["k"].shape[1],
+                         idx_heads=wl.idx_heads, idx_dim=wl.idx_dim, top_k=wl.top_k, heads=wl.heads,
+                         kv_heads=wl.kv_heads, head_dim=wl.head_dim, scale=wl.scale,
+                         dtype=dsa.DSA_BF16 if wl.dtype == "bf16" else dsa.DSA_FP32)
+    ws = torch.empty(max(dsa.workspace_size(dims, dsa.DSA_OP_FORWARD_STREAM), 256), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(g["q"])
+    idx = {m: torch.empty((B, wl.n_q, wl.top_k), dtype=torch.int32, device=dev) for m in (False, True)}
+
+    def step(stream):
+        for (q0, nq, nkv) in calls:
+            sl = slice(q0 - wl.q_pos0, q0 - wl.q_pos0 + nq)
+            dsa.forward(g["qidx"][:, sl], g["w"][:, sl], g["kidx"], g["q"][:, sl], g["k"], g["v"],
+                        top_k=wl.top_k, q_pos0=q0, n_kv=nkv, scale=wl.scale, workspace=ws, out=out[:, sl],
+                        indices=idx[stream][:, sl], stream_select=stream)
+
+    ms = {}
+    for stream in (False, True, False, True):
+        step(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            step(stream)
+        torch.cuda.synchronize()
+        ms[stream] = 1e3 * (time.perf_counter() - t0) / reps
+    same = bool(torch.equal(idx[False], idx[True]))
+    del g, out, idx, ws
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "materialised_ms_per_step": round(ms[False], 4),
+            "streamed_ms_per_step": round(ms[True], 4), "streamed_speedup": round(ms[False] / ms[True], 3),
+            "indices_identical": same, "reps": reps}
+
+
 def cpu_baseline(wl, budget_s, torch, make_inputs):
     """The oracle as it stands, on seeded rows of the same workload, until the
     time budget is spent. Inputs are drawn on the host with the same recipe."""
@@ -451,6 +496,12 @@ def main():
         log(f"[bench] fp8 indexer on {name}: {r['fp8_index_ms_per_step']} ms vs bf16 "
             f"{r['bf16_index_ms_per_step']} ms, recall mean {r['selection_recall_mean']}")
         fp8_study.append(r)
+    stream_study = []
+    for name in [s_ for s_ in args.stream_study.split(",") if s_]:
+        r = stream_select_study(WORKLOADS[name], 3, torch, dsa, make_inputs)
+        log(f"[bench] streamed selection on {name}: {r['streamed_ms_per_step']} ms vs materialised "
+            f"{r['materialised_ms_per_step']} ms, indices identical {r['indices_identical']}")
+        stream_study.append(r)
     if args.copy_calibration:
         # one plain streaming kernel of known size (2^28 float32: 1 GiB read,
         # 1 GiB written) as the reference reading for the HBM byte counters
@@ -489,6 +540,7 @@ def main():
         "secondary": secondary,
         "front_end": front_end,
         "fp8_indexer": fp8_study,
+        "stream_select": stream_study,
         "device": torch.cuda.get_device_name(0),
     }
     text = json.dumps(line)

@@ -22,7 +22,7 @@ import torch  # imported before libdsa.so so both resolve to one HIP runtime
 
 __all__ = [
     "DsaError", "DSA_OP_INDEX_SCORES", "DSA_OP_TOPK_MASK", "DSA_OP_SPARSE_ATTENTION",
-    "DSA_OP_FORWARD", "library_path", "lib", "make_dims", "index_scores", "topk_mask",
+    "DSA_OP_FORWARD", "DSA_OP_FORWARD_STREAM", "library_path", "lib", "make_dims", "index_scores", "topk_mask",
     "sparse_attention", "forward", "forward_varlen", "indexer_project", "ProjDims",
     "make_proj_dims", "proj_workspace_size", "quantize_fp8", "quantize_keys_fp8", "index_scores_fp8",
     "workspace_size", "lpad",
@@ -33,6 +33,7 @@ library_path = os.path.join(_HERE, "libdsa.so")
 
 DSA_FP32, DSA_BF16 = 0, 1
 DSA_OP_INDEX_SCORES, DSA_OP_TOPK_MASK, DSA_OP_SPARSE_ATTENTION, DSA_OP_FORWARD = 0, 1, 2, 3
+DSA_OP_FORWARD_STREAM = 4
 
 
 class DsaError(RuntimeError):
@@ -67,6 +68,8 @@ _SIGS = {
                                             ctypes.c_size_t, _P]),
     "dsa_forward": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    _P, ctypes.c_size_t, _P]),
+    "dsa_forward_stream_select": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                                 _P, _P, ctypes.c_size_t, _P]),
     "dsa_forward_varlen": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, ctypes.c_size_t, _P]),
     "dsa_quantize_fp8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P]),
@@ -231,7 +234,7 @@ def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=Fals
 
 def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
             return_indices=True, return_mask=False, return_lse=False, workspace=None, out=None,
-            indices=None, mask=None, lse=None, seq_lens=None):
+            indices=None, mask=None, lse=None, seq_lens=None, stream_select=False):
     """The whole DSA layer. Returns a dict with 'out' and the requested extras
     ('indices' [B, T, top_k] int32, 'mask' [B, T, Lpad/32] int32, 'lse').
     Passing `out`, `indices`, `mask`, `lse` or `workspace` tensors makes the
@@ -239,7 +242,9 @@ def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
     returned). With `seq_lens` (int32 [B] on the GPU) the call goes to
     dsa_forward_varlen: sequence b has seq_lens[b] cached tokens and its
     queries are its last T positions; `n_kv` (default: the caches' capacity)
-    is the longest sequence and `q_pos0` is ignored."""
+    is the longest sequence and `q_pos0` is ignored. With `stream_select` the
+    call goes to dsa_forward_stream_select (the same results; long rows take
+    their selection from survivor lists instead of stored scores)."""
     _need_gpu(qidx, w, kidx, q, k, v, workspace, out, indices, mask, lse, seq_lens)
     B, T, HI, DI = qidx.shape
     H, D = q.shape[2], q.shape[3]
@@ -269,11 +274,15 @@ def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
             res[name] = given
         elif wanted:
             res[name] = torch.empty(shape, dtype=dt, device=dev)
-    ws, nbytes = _workspace(d, DSA_OP_FORWARD, dev, workspace)
+    if stream_select and seq_lens is not None:
+        raise ValueError("stream_select applies to prefill-shaped calls, not varlen decode batches")
+    ws, nbytes = _workspace(d, DSA_OP_FORWARD_STREAM if stream_select else DSA_OP_FORWARD, dev, workspace)
     tail = (_ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k), _ptr(v), _ptr(res["out"]),
             _ptr(res.get("lse")), _ptr(res.get("indices")), _ptr(res.get("mask")), _ptr(ws), nbytes,
             _stream(q))
-    if seq_lens is None:
+    if stream_select:
+        _check(lib().dsa_forward_stream_select(ctypes.byref(d), *tail))
+    elif seq_lens is None:
         _check(lib().dsa_forward(ctypes.byref(d), *tail))
     else:
         _check(lib().dsa_forward_varlen(ctypes.byref(d), _ptr(seq_lens), *tail))

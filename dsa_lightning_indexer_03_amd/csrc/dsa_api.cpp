@@ -149,17 +149,47 @@ AttnWs attn_ws(const dsa_dims& d, bool have_list) {
   return w;
 }
 
+// Streaming selection: prefill-shaped calls with many long rows score a
+// sample of each row first (every kStreamStride-th 64-key tile), guess each
+// row's survivor threshold from it, and have the indexer keep only the
+// (key, token) pairs reaching the guess (at most kStreamCap per row) instead
+// of storing every score; rows the lists cannot decide take the
+// materialised scores and top-k (their query tiles only).
+constexpr int kStreamStride = 16;
+constexpr int kStreamCap = 8192;
+bool use_stream_select(const dsa_dims& d) {
+  const int64_t rows = (int64_t)d.batch * d.n_q;
+  return d.n_q > 8 && (int64_t)d.q_pos0 + d.n_q > 16384 && d.n_kv <= dsa::kTopkMaxRow && d.top_k <= 2048 &&
+         rows >= 512;
+}
+int stream_sample_ld(const dsa_dims& d) { return (d.n_kv + 64 * kStreamStride - 1) / (64 * kStreamStride) * 64; }
+int stream_nqt(const dsa_dims& d) { return (d.n_q + dsa::kIdxQueryTile - 1) / dsa::kIdxQueryTile; }
+
 struct FwdWs {
   size_t scores = 0, mask = 0, indices = 0, attn = 0, total = 0;
+  // streaming selection: sampled scores, guesses, survivor lists, and the
+  // counters and flags (one contiguous block, zeroed per call)
+  size_t sample = 0, guess = 0, cand = 0, counters = 0, n_counters = 0;
   AttnWs aw;
 };
-FwdWs fwd_ws(const dsa_dims& d, bool user_mask, bool user_indices) {
+FwdWs fwd_ws(const dsa_dims& d, bool user_mask, bool user_indices, bool stream = false) {
   FwdWs w;
   const int64_t rows = (int64_t)d.batch * d.n_q;
   const int64_t lp = lpad_of(d);
   size_t off = 0;
   w.scores = off;
   off += align_up((size_t)rows * lp * 4);
+  if (stream && use_stream_select(d)) {
+    w.sample = off;
+    off += align_up((size_t)rows * stream_sample_ld(d) * 4);
+    w.guess = off;
+    off += align_up((size_t)rows * 4);
+    w.cand = off;
+    off += align_up((size_t)rows * kStreamCap * 8);
+    w.counters = off;
+    w.n_counters = (size_t)rows * 2 + (size_t)d.batch * stream_nqt(d);  // counts, row flags, tile flags
+    off += align_up(w.n_counters * 4);
+  }
   if (!user_mask) {
     w.mask = off;
     off += align_up((size_t)rows * (lp / 32) * 4);
@@ -176,8 +206,8 @@ FwdWs fwd_ws(const dsa_dims& d, bool user_mask, bool user_indices) {
   return w;
 }
 
-dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const void* kidx, float* scores,
-                      bool write_upper, hipStream_t st, const int32_t* seq_len = nullptr) {
+dsa::IndexerParams indexer_params(const dsa_dims& d, const void* qidx, const float* w, const void* kidx,
+                                  float* scores, bool write_upper, const int32_t* seq_len) {
   dsa::IndexerParams p{};
   p.qidx = qidx;
   p.w = w;
@@ -192,11 +222,17 @@ dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const
   p.Lpad = (int)lpad_of(d);
   p.write_upper = write_upper ? 1 : 0;
   p.seq_len = seq_len;
+  return p;
+}
+
+dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const void* kidx, float* scores,
+                      bool write_upper, hipStream_t st, const int32_t* seq_len = nullptr) {
+  const dsa::IndexerParams p = indexer_params(d, qidx, w, kidx, scores, write_upper, seq_len);
   return hip_status(dsa::launch_indexer(p, d.dtype, d.idx_dim, st), "indexer launch", st);
 }
 
 dsa_status run_topk(const dsa_dims& d, const float* scores, uint32_t* mask, int32_t* indices, hipStream_t st,
-                    const int32_t* seq_len = nullptr) {
+                    const int32_t* seq_len = nullptr, const uint32_t* row_flag = nullptr) {
   dsa::TopkParams p{};
   p.scores = scores;
   p.mask = mask;
@@ -208,7 +244,60 @@ dsa_status run_topk(const dsa_dims& d, const float* scores, uint32_t* mask, int3
   p.Lpad = (int)lpad_of(d);
   p.top_k = d.top_k;
   p.seq_len = seq_len;
+  p.row_flag = row_flag;
   return hip_status(dsa::launch_topk(p, st), "top-k launch", st);
+}
+
+// Scores and selection of a forward call whose rows are long: sampled
+// scores -> guesses -> survivor lists -> selection, then the materialised
+// path for the query tiles with undecided rows (both launches return at once
+// when there are none).
+dsa_status run_stream_select(const dsa_dims& d, const void* qidx, const float* w, const void* kidx, unsigned char* wsb,
+                             const FwdWs& fw, uint32_t* mask, int32_t* indices, hipStream_t st) {
+  const int64_t rows = (int64_t)d.batch * d.n_q;
+  uint32_t* counters = reinterpret_cast<uint32_t*>(wsb + fw.counters);
+  uint32_t* cand_count = counters;
+  uint32_t* row_flag = counters + rows;
+  uint32_t* tile_flag = counters + 2 * rows;
+  float* scores = reinterpret_cast<float*>(wsb + fw.scores);
+  dsa::StreamSelParams sp{};
+  sp.sample = reinterpret_cast<const float*>(wsb + fw.sample);
+  sp.sample_ld = stream_sample_ld(d);
+  sp.kt_stride = kStreamStride;
+  sp.guess = reinterpret_cast<uint32_t*>(wsb + fw.guess);
+  sp.cand = reinterpret_cast<const uint2*>(wsb + fw.cand);
+  sp.cand_count = cand_count;
+  sp.cand_cap = kStreamCap;
+  sp.row_flag = row_flag;
+  sp.tile_flag = tile_flag;
+  sp.nqt = stream_nqt(d);
+  sp.mask = mask;
+  sp.indices = indices;
+  sp.B = d.batch;
+  sp.T = d.n_q;
+  sp.q_pos0 = d.q_pos0;
+  sp.n_kv = d.n_kv;
+  sp.Lpad = (int)lpad_of(d);
+  sp.top_k = d.top_k;
+
+  dsa::IndexerParams ps = indexer_params(d, qidx, w, kidx, reinterpret_cast<float*>(wsb + fw.sample), false, nullptr);
+  ps.Lpad = sp.sample_ld;
+  ps.kt_stride = kStreamStride;
+  DSA_TRY(hip_status(dsa::launch_indexer(ps, d.dtype, d.idx_dim, st), "sampled indexer launch", st));
+  DSA_TRY(hip_status(dsa::launch_zero_u32(counters, fw.n_counters, st), "counter reset launch", st));
+  DSA_TRY(hip_status(dsa::launch_stream_guess(sp, st), "threshold guess launch", st));
+  dsa::IndexerParams pf = indexer_params(d, qidx, w, kidx, nullptr, false, nullptr);
+  pf.guess = sp.guess;
+  pf.cand = reinterpret_cast<uint2*>(wsb + fw.cand);
+  pf.cand_count = cand_count;
+  pf.cand_cap = kStreamCap;
+  DSA_TRY(hip_status(dsa::launch_indexer(pf, d.dtype, d.idx_dim, st), "filtering indexer launch", st));
+  DSA_TRY(hip_status(dsa::launch_stream_select(sp, st), "survivor selection launch", st));
+  dsa::IndexerParams pm = indexer_params(d, qidx, w, kidx, scores, false, nullptr);
+  pm.tile_flag = tile_flag;
+  DSA_TRY(hip_status(dsa::launch_indexer(pm, d.dtype, d.idx_dim, st), "indexer launch", st));
+  DSA_TRY(run_topk(d, scores, mask, indices, st, nullptr, row_flag));
+  return ok();
 }
 
 dsa_status run_attention(const dsa_dims& d, const void* q, const void* k, const void* v, const uint32_t* mask,
@@ -488,9 +577,9 @@ dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void*
   return ok();
 }
 
-dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx, const void* q,
-                       const void* k_cache, const void* v_cache, void* out, float* lse, int32_t* indices,
-                       uint32_t* mask, void* ws, size_t ws_bytes, void* stream) {
+static dsa_status forward_impl(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx, const void* q,
+                        const void* k_cache, const void* v_cache, void* out, float* lse, int32_t* indices,
+                        uint32_t* mask, void* ws, size_t ws_bytes, void* stream, bool stream_select) {
   DSA_TRY(check_dims(dims, true, true, true));
   DSA_TRY(check_ptr(qidx, "qidx"));
   DSA_TRY(check_ptr(w, "w"));
@@ -503,7 +592,7 @@ dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, c
   DSA_TRY(check_ptr(indices, "indices", false));
   DSA_TRY(check_ptr(mask, "mask", false));
   const dsa_dims& d = *dims;
-  const FwdWs fw = fwd_ws(d, mask != nullptr, indices != nullptr);
+  const FwdWs fw = fwd_ws(d, mask != nullptr, indices != nullptr, stream_select);
   DSA_TRY(check_ptr(ws, "workspace"));
   if (ws_bytes < fw.total) return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, fw.total);
   hipStream_t st = (hipStream_t)stream;
@@ -513,11 +602,29 @@ dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, c
   const bool gather = use_gather(d);
   const bool mqa = use_mqa_list(d);
   int32_t* idx = indices ? indices : (gather || mqa ? reinterpret_cast<int32_t*>(wsb + fw.indices) : nullptr);
-  DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
-  DSA_TRY(run_topk(d, scores, m, idx, st));
+  if (stream_select && use_stream_select(d)) {
+    DSA_TRY(run_stream_select(d, qidx, w, kidx, wsb, fw, m, idx, st));
+  } else {
+    DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
+    DSA_TRY(run_topk(d, scores, m, idx, st));
+  }
   DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather || mqa ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw,
                         st));
   return ok();
+}
+
+dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx, const void* q,
+                       const void* k_cache, const void* v_cache, void* out, float* lse, int32_t* indices,
+                       uint32_t* mask, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(dims, qidx, w, kidx, q, k_cache, v_cache, out, lse, indices, mask, ws, ws_bytes, stream,
+                      false);
+}
+
+dsa_status dsa_forward_stream_select(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
+                                     const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                     int32_t* indices, uint32_t* mask, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(dims, qidx, w, kidx, q, k_cache, v_cache, out, lse, indices, mask, ws, ws_bytes, stream,
+                      true);
 }
 
 dsa_status dsa_forward_varlen(const dsa_dims* dims, const int32_t* seq_lens, const void* qidx, const float* w,
@@ -570,6 +677,9 @@ size_t dsa_workspace_size(const dsa_dims* dims, int32_t op) {
     case DSA_OP_FORWARD:
       if (check_dims(dims, true, true, true) != DSA_OK) return 0;
       return fwd_ws(d, false, false).total;
+    case DSA_OP_FORWARD_STREAM:
+      if (check_dims(dims, true, true, true) != DSA_OK) return 0;
+      return fwd_ws(d, false, false, true).total;
     default:
       return 0;
   }

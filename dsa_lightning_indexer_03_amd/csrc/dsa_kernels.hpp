@@ -17,7 +17,18 @@ struct IndexerParams {
   int write_upper;    // 1: write -inf for s > p; 0: leave those entries untouched
   const int32_t* seq_len;  // [B] per-sequence cache lengths (decode kernel only), or nullptr
   const float* kscale;     // fp8 keys: [B][kv_cap] per-key scales; nullptr otherwise
+  // Streaming selection (prefill kernel only; zero / nullptr: plain scores).
+  int kt_stride;              // > 1: score only key tiles kt_stride * j (a sample), stored
+                              // compactly at column 64 j + (s mod 64)
+  const uint32_t* guess;      // [B*T] survivor threshold on key >> 10; set: no scores are stored,
+                              // survivors go to cand instead
+  uint2* cand;                // [B*T][cand_cap] (orderable key, token) of the survivors
+  uint32_t* cand_count;       // [B*T] survivors found (may exceed cand_cap; only cand_cap are written)
+  int cand_cap;
+  const uint32_t* tile_flag;  // [B][query tiles of 32]: a workgroup scores its range only when
+                              // one of the range's query tiles is flagged; nullptr: always
 };
+constexpr int kIdxQueryTile = 32;  // queries per prefill indexer query tile
 // dtype: 0 fp32, 1 bf16, kIndexerFp8 e4m3 codes (qidx, kidx; w holds the
 // query-scaled weights, kscale the key scales; DI 128 only)
 constexpr int kIndexerFp8 = 2;
@@ -63,8 +74,32 @@ struct TopkParams {
   int32_t* indices;     // [B][T][top_k] or nullptr
   int B, T, q_pos0, n_kv, Lpad, top_k;
   const int32_t* seq_len;  // [B] per-sequence cache lengths, or nullptr
+  const uint32_t* row_flag;  // [B*T]: select only rows whose flag is nonzero; nullptr: all rows
 };
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
+
+// Streaming selection for long prefill rows (topk.hip): the survivor
+// threshold of each row from its sampled scores, and the exact selection
+// from each row's survivor list. Rows the lists cannot decide are flagged
+// (row_flag, and tile_flag of their query tile) for the materialised path.
+struct StreamSelParams {
+  const float* sample;      // [B*T][sample_ld] sampled scores (key tiles kt_stride * j)
+  int sample_ld, kt_stride;
+  uint32_t* guess;          // [B*T]
+  const uint2* cand;        // [B*T][cand_cap]
+  const uint32_t* cand_count;
+  int cand_cap;
+  uint32_t* row_flag;       // [B*T]
+  uint32_t* tile_flag;      // [B][nqt]
+  int nqt;
+  uint32_t* mask;           // [B*T][Lpad/32]
+  int32_t* indices;         // [B*T][top_k] or nullptr
+  int B, T, q_pos0, n_kv, Lpad, top_k;
+};
+hipError_t launch_stream_guess(const StreamSelParams& p, hipStream_t st);
+hipError_t launch_stream_select(const StreamSelParams& p, hipStream_t st);
+// zeroes n words (counters and flags; a kernel, not a memset node)
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st);
 
 // Masked flash attention over 64-key tiles (prefill-shaped calls).
 struct AttnParams {

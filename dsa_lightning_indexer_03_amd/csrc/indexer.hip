@@ -140,21 +140,23 @@ constexpr int kIdxQT = kIdxWaves * QPW;      // 32 queries per query tile
 constexpr int kIdxKT = DSA_IDX_KT;            // keys per key tile
 static_assert(kIdxKT % kIdxQT == 0, "query tile divides key tile");
 
+static_assert(kIdxQT == kIdxQueryTile, "query tile size shared with the host");
+
 struct UnitMap {
-  int T, q_pos0, nqt, nfull;
+  int T, q_pos0, nqt, nfull, ktw;  // ktw: keys spanned by one unit's key tile (kIdxKT x stride)
   long long per_seq;
-  __device__ __host__ int ntk(int qt) const { return (q_pos0 + min(kIdxQT * qt + kIdxQT - 1, T - 1)) / kIdxKT + 1; }
-  // sum over x < n of floor(x / R), R = key tile / query tile
-  __device__ __host__ static long long floor_sum(long long n) {
-    constexpr int R = kIdxKT / kIdxQT;
+  __device__ __host__ int ntk(int qt) const { return (q_pos0 + min(kIdxQT * qt + kIdxQT - 1, T - 1)) / ktw + 1; }
+  // sum over x < n of floor(x / R), R = ktw / query tile
+  __device__ __host__ long long floor_sum(long long n) const {
+    const int R = ktw / kIdxQT;
     const long long m = n / R;
     return R * m * (m - 1) / 2 + (n - R * m) * m;
   }
   // units of query tiles 0..n-1. A full query tile qt has
-  // floor((A + QT qt) / KT) + 1 key tiles, A = q_pos0 + QT - 1; with
-  // A = a0 KT + rq QT + rr (rr < QT) that is a0 + 1 + floor((qt + rq) / R).
+  // floor((A + QT qt) / ktw) + 1 key tiles, A = q_pos0 + QT - 1; with
+  // A = a0 ktw + rq QT + rr (rr < QT) that is a0 + 1 + floor((qt + rq) / R).
   __device__ __host__ long long prefix(int n) const {
-    const int A = q_pos0 + kIdxQT - 1, a0 = A / kIdxKT, rq = (A % kIdxKT) / kIdxQT;
+    const int A = q_pos0 + kIdxQT - 1, a0 = A / ktw, rq = (A % ktw) / kIdxQT;
     const long long k = min(n, nfull);
     long long s = k * (a0 + 1) + floor_sum(rq + k) - floor_sum(rq);
     if (n > nfull) s += ntk(nfull);
@@ -169,9 +171,11 @@ struct UnitMap {
   __device__ __host__ long long prefix_pos(int n) const {
     return prefix((n + 1) >> 1) + per_seq - prefix(nqt - (n >> 1));
   }
-  __device__ __host__ void init(int T_, int q_pos0_) {
+  // stride > 1: only every stride-th key tile (a sample of the keys)
+  __device__ __host__ void init(int T_, int q_pos0_, int stride = 1) {
     T = T_;
     q_pos0 = q_pos0_;
+    ktw = kIdxKT * (stride > 1 ? stride : 1);
     nqt = (T + kIdxQT - 1) / kIdxQT;
     nfull = T / kIdxQT;
     per_seq = prefix(nqt);
@@ -245,7 +249,8 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // lanes reading one chunk column of 16 consecutive rows hit distinct banks.
 // The scores of a unit are stored one unit late, after the next tile loads
 // are issued.
-template <typename T, int DI>
+// STREAM: survivor lists instead of stored scores (a.guess set)
+template <typename T, int DI, bool STREAM>
 __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(IndexerParams a, UnitMap um,
                                                                           long long n_units) {
   constexpr int KT = kIdxKT, KSTEPS = DI / kStepElems<T>, NSUB = KT / 16, S = kIdxStages;
@@ -269,6 +274,21 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   const long long u0 = (long long)r * n_units / G;
   const long long u1 = (long long)(r + 1) * n_units / G;
   if (u0 >= u1) return;
+  if (a.tile_flag) {  // score the range only when one of its query tiles is flagged
+    int fb, fpos, fkt;
+    um.decode(u0, fb, fpos, fkt);
+    bool any = false;
+    for (long long tu = u0; tu < u1;) {
+      any = any || a.tile_flag[fb * um.nqt + um.qt_at(fpos)] != 0u;
+      tu = (long long)fb * um.per_seq + um.prefix_pos(fpos + 1);  // first unit of the next tile
+      if (++fpos == um.nqt) {
+        fpos = 0;
+        ++fb;
+      }
+    }
+    if (!any) return;
+  }
+  const int kstride = a.kt_stride > 1 ? a.kt_stride : 1;  // key tiles scored: kstride * kt
   const float ninf = fneg_inf();
   const int jl = ((g & 1) << 1) | (g >> 1);  // query of the wave whose score this lane ends up with
 
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   }
   const char* kcache = static_cast<const char*>(a.kidx);
   auto dload = [&](int b, int kt, int slot) {
-    const int s0 = kt * KT;
+    const int s0 = kt * kstride * KT;
     const char* kb = kcache + ((size_t)b * a.kv_cap + s0) * ROWB;
     unsigned char* dst = lds + slot * SLOT;
     if constexpr (kFp8) dma4(a.kscale + (size_t)b * a.kv_cap + min(s0 + lane, a.n_kv - 1), dst + TILEB + wave_u * 256);
@@ -351,15 +371,50 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   // scores of the previous unit, stored one unit late
   float pend[NSUB];
   float* pend_row = nullptr;
-  int pend_s0 = 0, pend_p = 0;
+  int pend_s0 = 0, pend_c0 = 0, pend_p = 0;
+  // streaming selection: this lane's row (or -1) and its survivor threshold
+  int row_mine = -1, pend_rowid = -1;
+  uint32_t guess_mine = 0, pend_guess = 0;
   auto flush = [&]() {
-    if (pend_row) {
+    if constexpr (STREAM) {
+      // survivors (key prefix reaching the row's guess) appended to the row's
+      // list: ranks within the 16 lanes of one query, one atomic per row and unit
+      uint32_t keys[NSUB];
+      uint32_t cnt = 0;
 #pragma unroll
       for (int sub = 0; sub < NSUB; ++sub) {
         const int s = pend_s0 + sub * 16 + c;
+        keys[sub] = orderable_key(pend[sub]);
+        const bool sv = pend_rowid >= 0 && s <= pend_p && (keys[sub] >> 10) >= pend_guess;
+        if (!sv) keys[sub] = 0u;
+        cnt += sv ? 1u : 0u;
+      }
+      uint32_t incl = cnt;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 16);
+        if (c >= off) incl += o;
+      }
+      const uint32_t total = (uint32_t)__shfl((int)incl, 15, 16);
+      uint32_t base = 0;
+      if (c == 15 && total > 0u) base = atomicAdd(a.cand_count + pend_rowid, total);
+      base = (uint32_t)__shfl((int)base, 15, 16);
+      uint32_t at = base + incl - cnt;
+      uint2* lst = a.cand + (size_t)max(pend_rowid, 0) * a.cand_cap;
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        if (keys[sub] != 0u) {
+          if (at < (uint32_t)a.cand_cap) lst[at] = make_uint2(keys[sub], (uint32_t)(pend_s0 + sub * 16 + c));
+          ++at;
+        }
+      }
+    } else if (pend_row) {
+#pragma unroll
+      for (int sub = 0; sub < NSUB; ++sub) {
+        const int s = pend_s0 + sub * 16 + c, col = pend_c0 + sub * 16 + c;
         // scores are streamed out with non-temporal stores (read once, by top-k)
-        if (s <= pend_p) __builtin_nontemporal_store(pend[sub], pend_row + s);
-        else if (a.write_upper) __builtin_nontemporal_store(ninf, pend_row + s);
+        if (s <= pend_p) __builtin_nontemporal_store(pend[sub], pend_row + col);
+        else if (a.write_upper) __builtin_nontemporal_store(ninf, pend_row + col);
       }
     }
   };
@@ -381,7 +436,11 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
       const int t_mine = t_wave + jl;
       p_mine = a.q_pos0 + t_mine;
-      srow = t_mine < a.T ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
+      srow = t_mine < a.T && !STREAM ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
+      if constexpr (STREAM) {
+        row_mine = t_mine < a.T ? b * a.T + t_mine : -1;
+        guess_mine = row_mine >= 0 ? a.guess[row_mine] : 0u;
+      }
     }
     // stores of unit u-1, then the tile of unit u+S-1 (or the range's last
     // one again) into the slot read at unit u-1: the newest S-2 tile loads
@@ -393,7 +452,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     }
     dload(pb, pkt, slot == 0 ? S - 1 : slot - 1);
 
-    const int s_tile = kt * KT;
+    const int s_tile = kt * kstride * KT;
     float cur[NSUB];
 #pragma unroll
     for (int sub = 0; sub < NSUB; ++sub) {
@@ -410,7 +469,10 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     for (int sub = 0; sub < NSUB; ++sub) pend[sub] = cur[sub];
     pend_row = srow;
     pend_s0 = s_tile;
+    pend_c0 = kt * KT;
     pend_p = p_mine;
+    pend_rowid = row_mine;
+    pend_guess = guess_mine;
 
     // Tile u+1 has landed in every wave's part (each wave waits for its own
     // loads; the S-2 tiles issued after it may still be in flight) before
@@ -433,7 +495,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
 // 0..ntk(qt)-1 only). One workgroup per query row.
 __global__ __launch_bounds__(256) void scores_upper_fill_kernel(IndexerParams a, UnitMap um) {
   const int row = blockIdx.x, t = row % a.T;
-  const int s_from = um.ntk(t / kIdxQT) * kIdxKT;
+  const int s_from = um.ntk(t / kIdxQT) * um.ktw;
   float* srow = a.scores + (size_t)row * a.Lpad;
   const float ninf = fneg_inf();
   for (int s4 = s_from + 4 * threadIdx.x; s4 < a.Lpad; s4 += 4 * 256)
@@ -527,7 +589,7 @@ hipError_t launch_indexer_t(const IndexerParams& p, hipStream_t st) {
     hipLaunchKernelGGL((indexer_decode_kernel<T, DI, QPW>), grid, dim3(256), 0, st, q);
   } else {
     UnitMap um;
-    um.init(p.T, p.q_pos0);
+    um.init(p.T, p.q_pos0, p.kt_stride);
     const long long n_units = um.per_seq * p.B;
     if (p.write_upper) {
       hipLaunchKernelGGL(scores_upper_fill_kernel, dim3(p.B * p.T), dim3(256), 0, st, q, um);
@@ -535,7 +597,11 @@ hipError_t launch_indexer_t(const IndexerParams& p, hipStream_t st) {
       if (e != hipSuccess) return e;
     }
     const int n_wg = (int)std::min<long long>(n_units, (long long)device_cu_count() * DSA_IDX_WG_PER_CU);
-    hipLaunchKernelGGL((indexer_prefill_kernel<T, DI>), dim3(n_wg), dim3(64 * kIdxWaves), 0, st, q, um, n_units);
+    if (p.guess)
+      hipLaunchKernelGGL((indexer_prefill_kernel<T, DI, true>), dim3(n_wg), dim3(64 * kIdxWaves), 0, st, q, um, n_units);
+    else
+      hipLaunchKernelGGL((indexer_prefill_kernel<T, DI, false>), dim3(n_wg), dim3(64 * kIdxWaves), 0, st, q, um,
+                         n_units);
   }
   return hipGetLastError();
 }

@@ -12,6 +12,7 @@ namespace {
 
 template <int NW, int EPT_R, int EPT_L>
 __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
+  if (a.row_flag && a.row_flag[(size_t)blockIdx.y * a.T + blockIdx.x] == 0u) return;
   __shared__ TopkShared<NW, EPT_L> sh;
   topk_select_row<NW, EPT_R, EPT_L>(a, blockIdx.x, blockIdx.y, sh);
 }
@@ -80,8 +81,8 @@ __device__ __forceinline__ uint32_t ordered_positions(const uint64_t (&bal)[kLon
 // (key 0 = no token, never counted). Returns the threshold as (thr, shift):
 // the tokens kept are key >> shift > thr, plus, among key >> shift == thr,
 // all of them when all_eq, else the first `rem` in index order.
-template <typename ForEach>
-__device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t rank, TopkLongShared& sh,
+template <typename ForEach, typename Sh>
+__device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t rank, Sh& sh,
                                                   uint32_t& thr, int& shift_out, uint32_t& rem, bool& all_eq) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, count_eq = 0;
@@ -131,6 +132,7 @@ __device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t ran
 }
 
 __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) void topk_long_kernel(TopkParams a) {
+  if (a.row_flag && a.row_flag[(size_t)blockIdx.y * a.T + blockIdx.x] == 0u) return;
   __shared__ TopkLongShared sh;
   const int t = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -323,6 +325,136 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
     *reinterpret_cast<uint2*>(mrow + 2 * wp) = make_uint2(0u, 0u);
 }
 
+
+// Streaming selection for long prefill rows: the indexer first scores a
+// sample of each row (every kt_stride-th 64-key tile); stream_guess_kernel
+// turns it into the row's survivor threshold (as the streamed top-k above
+// does with its sample); the indexer then stores only the (key, token)
+// pairs reaching it, and stream_select_kernel selects from that list. The
+// list holds every token whose score can be among the row's top_k as soon
+// as it has at least top_k entries, so the selection is exact; rows with
+// fewer (an unrepresentative sample) or more than the list holds are
+// flagged, with their query tile, for the materialised scores and top-k.
+struct StreamShared {
+  uint32_t hist[2048];  // radix histograms, then the mask bitmap
+  uint32_t red[kLongNW];
+  uint32_t found[3];
+};
+
+__global__ __launch_bounds__(kLongNT) void stream_guess_kernel(StreamSelParams a) {
+  __shared__ StreamShared sh;
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t row = (size_t)b * a.T + t;
+  const int p = a.q_pos0 + t, n = p + 1;
+  const uint32_t k = (uint32_t)a.top_k;
+  if (k >= (uint32_t)n || n <= a.cand_cap) {  // every token survives (or every token is kept)
+    if (tid == 0) a.guess[row] = 0u;
+    return;
+  }
+  const int span = 64 * a.kt_stride;  // tokens between sampled tiles
+  const float* srow = a.sample + row * a.sample_ld;
+  uint32_t skey[kLongEPT];
+#pragma unroll
+  for (int e = 0; e < kLongEPT; ++e) {
+    const int j = e * kLongNT + tid;
+    const int s = (j >> 6) * span + (j & 63);
+    skey[e] = j < a.sample_ld && s <= p ? orderable_key(srow[min(j, a.sample_ld - 1)]) : 0u;
+  }
+  const int kt0 = p / span;  // last sampled tile at or before p
+  const uint32_t nsv = (uint32_t)(64 * kt0 + min(p - kt0 * span + 1, 64));  // sampled tokens
+  const uint32_t ks = min(nsv, (uint32_t)((1.25f * (float)k * (float)nsv) / (float)n) + 16u);
+  uint32_t thr, rem;
+  int shift;
+  bool all_eq;
+  long_radix_select([&](auto f) {
+#pragma unroll
+    for (int e = 0; e < kLongEPT; ++e) f(skey[e]);
+  }, ks, sh, thr, shift, rem, all_eq);
+  if (tid == 0) a.guess[row] = shift >= 10 ? thr << (shift - 10) : thr >> (10 - shift);
+}
+
+__global__ __launch_bounds__(kLongNT) void stream_select_kernel(StreamSelParams a) {
+  __shared__ StreamShared sh;
+  const int t = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const size_t row = (size_t)b * a.T + t;
+  const int p = a.q_pos0 + t, n = p + 1;
+  const int nwords = a.Lpad / 32;
+  uint32_t* mrow = a.mask + row * nwords;
+  int32_t* irow = a.indices ? a.indices + row * a.top_k : nullptr;
+  const uint32_t k = (uint32_t)a.top_k;
+  if (k >= (uint32_t)n) {  // every candidate is kept
+    for (int wi = tid; wi < nwords; wi += kLongNT) {
+      const int lo = wi * 32;
+      mrow[wi] = lo + 32 <= n ? 0xffffffffu : (lo < n ? (1u << (n - lo)) - 1u : 0u);
+    }
+    if (irow)
+      for (int j = tid; j < a.top_k; j += kLongNT) irow[j] = j < n ? j : -1;
+    return;
+  }
+  const uint32_t cnt = a.cand_count[row];
+  if (cnt < k || cnt > (uint32_t)a.cand_cap) {
+    if (tid == 0) {
+      a.row_flag[row] = 1u;
+      a.tile_flag[(size_t)b * a.nqt + t / kIdxQueryTile] = 1u;
+    }
+    return;
+  }
+  const uint2* lst = a.cand + row * a.cand_cap;
+  // k-th largest key among the survivors
+  uint32_t thr, rem;
+  int shift;
+  bool all_eq;
+  long_radix_select([&](auto f) {
+    for (uint32_t j = tid; j < cnt; j += kLongNT) f(lst[j].x);
+  }, k, sh, thr, shift, rem, all_eq);
+  // ties at the threshold: the rem lowest tokens, i.e. the rem largest of
+  // 65536 - token among the threshold-equal survivors (tokens are distinct)
+  uint32_t tthr = 0;
+  int tshift = 0;
+  if (!all_eq) {
+    uint32_t trem;
+    bool tall;
+    long_radix_select([&](auto f) {
+      for (uint32_t j = tid; j < cnt; j += kLongNT) {
+        const uint2 e = lst[j];
+        f((e.x >> shift) == thr ? 65536u - e.y : 0u);
+      }
+    }, rem, sh, tthr, tshift, trem, tall);
+  }
+  for (int i = tid; i < nwords; i += kLongNT) sh.hist[i] = 0u;  // bitmap
+  __syncthreads();
+  for (uint32_t j = tid; j < cnt; j += kLongNT) {
+    const uint2 e = lst[j];
+    const uint32_t hk = e.x >> shift;
+    const bool sel = hk > thr || (hk == thr && (all_eq || ((65536u - e.y) >> tshift) >= tthr));
+    if (sel) atomicOr(&sh.hist[e.y >> 5], 1u << (e.y & 31));
+  }
+  __syncthreads();
+  for (int i = tid; i < nwords; i += kLongNT) mrow[i] = sh.hist[i];
+  if (irow) {  // ascending: each thread takes a run of consecutive words
+    constexpr int WPT = 2048 / kLongNT;
+    const int w0 = tid * WPT;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) c += w0 + i < nwords ? (uint32_t)__popc(sh.hist[w0 + i]) : 0u;
+    uint32_t pos = block_inclusive_sum<kLongNW>(c, sh.red) - c;
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      uint32_t bits = w0 + i < nwords ? sh.hist[w0 + i] : 0u;
+      while (bits) {
+        const int bit = __ffs(bits) - 1;
+        if (pos < k) irow[pos] = 32 * (w0 + i) + bit;
+        ++pos;
+        bits &= bits - 1u;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
@@ -352,6 +484,25 @@ hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
     hipLaunchKernelGGL((topk_mask_kernel<16, 32, 32>), grid, dim3(1024), 0, st, p);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_guess(const StreamSelParams& p, hipStream_t st) {
+  if (p.sample_ld > kLongEPT * kLongNT || p.q_pos0 + p.T > kTopkMaxRow) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_guess_kernel, dim3(p.T, p.B), dim3(kLongNT), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_select(const StreamSelParams& p, hipStream_t st) {
+  if (p.Lpad > 2048 * 32 || p.q_pos0 + p.T > kTopkMaxRow) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_select_kernel, dim3(p.T, p.B), dim3(kLongNT), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

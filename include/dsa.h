@@ -74,7 +74,8 @@ typedef enum {
   DSA_OP_INDEX_SCORES = 0,
   DSA_OP_TOPK_MASK = 1,
   DSA_OP_SPARSE_ATTENTION = 2,
-  DSA_OP_FORWARD = 3
+  DSA_OP_FORWARD = 3,
+  DSA_OP_FORWARD_STREAM = 4
 } dsa_op;
 
 /* Problem sizes of one call.
@@ -172,6 +173,27 @@ dsa_status dsa_forward_varlen(const dsa_dims* dims, const int32_t* seq_lens, con
                               const void* k_cache, const void* v_cache, void* out, float* lse,
                               int32_t* indices, uint32_t* mask, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* The whole layer, as dsa_forward, with the selection streamed instead of
+ * materialised for calls with long rows: matching every cached key against
+ * the queries is the cost the layer keeps [aiu "Why it matters"; devotd
+ * section 4], and storing every score only to keep top_k of them per row is
+ * traffic on top of it. Calls with n_q > 8, more than 16384 candidates in the
+ * longest row, n_kv <= 65536, top_k <= 2048 and at least 512 query rows
+ * (others run exactly as dsa_forward): the indexer scores every 16th 64-key
+ * tile of each row first; a threshold guessed from that sample lets the
+ * indexer keep only the (score, token) pairs reaching it (at most 8192 per
+ * row) instead of storing every score; the selection is taken from those
+ * lists, and rows they cannot decide (fewer than top_k or more than 8192
+ * survivors) are scored and selected the materialised way, their query tiles
+ * only. The kept sets are exactly dsa_forward's (both select from the same
+ * float32 scores with the same tie rule), so every output is identical.
+ * Needs dsa_workspace_size(dims, DSA_OP_FORWARD_STREAM) bytes of workspace;
+ * every other argument, layout and error behaviour is dsa_forward's. */
+dsa_status dsa_forward_stream_select(const dsa_dims* dims, const void* qidx, const float* w,
+                                     const void* kidx, const void* q, const void* k_cache,
+                                     const void* v_cache, void* out, float* lse, int32_t* indices,
+                                     uint32_t* mask, void* ws, size_t ws_bytes, void* stream);
 
 /* fp8 reading of the indexer (a precision study: the pages keep the
  * indexer's tensors unquantised because top-k selection is sensitive to their

@@ -126,6 +126,23 @@ def test_workspace_sizes():
     assert dsa.workspace_size(_dims(n_q=0), dsa.DSA_OP_FORWARD) == 0
 
 
+def test_stream_select_workspace():
+    """The streamed selection needs room only for calls it applies to (>= 512
+    rows, longest row past 16384 candidates, top_k <= 2048): sampled scores
+    (every 16th 64-key tile), guesses, 8192-entry survivor lists, counters and
+    flags on top of the materialised layout."""
+    small = _dims(n_q=64, n_kv=100, kv_capacity=128)
+    assert dsa.workspace_size(small, dsa.DSA_OP_FORWARD_STREAM) == dsa.workspace_size(small, dsa.DSA_OP_FORWARD)
+    B, T, p0, L = 1, 1024, 20000, 21024
+    d = _dims(batch=B, n_q=T, q_pos0=p0, n_kv=L, kv_capacity=L, top_k=2048)
+    rows, sample_ld, nqt = B * T, (L + 1023) // 1024 * 64, (T + 31) // 32
+    al = lambda x: (x + 255) // 256 * 256
+    extra = al(rows * sample_ld * 4) + al(rows * 4) + al(rows * 8192 * 8) + al((2 * rows + B * nqt) * 4)
+    assert dsa.workspace_size(d, dsa.DSA_OP_FORWARD_STREAM) == dsa.workspace_size(d, dsa.DSA_OP_FORWARD) + extra
+    big_k = _dims(batch=B, n_q=T, q_pos0=p0, n_kv=L, kv_capacity=L, top_k=4096)
+    assert dsa.workspace_size(big_k, dsa.DSA_OP_FORWARD_STREAM) == dsa.workspace_size(big_k, dsa.DSA_OP_FORWARD)
+
+
 def test_binding_refuses_host_tensors():
     """No CPU fallback: the binding raises instead of computing on the host."""
     q = torch.zeros(1, 4, 32, 128, dtype=torch.bfloat16)

@@ -335,6 +335,53 @@ def test_topk_long_rows_streamed(case):
         assert np.array_equal(m_h[j], pack_mask(sel, n_kv)), f"{name} row {i} mask"
 
 
+STREAM_SEL = [
+    # name, B, T, q_pos0, top_k, recipe: forward calls with >= 512 rows and
+    # rows past 16384 tokens select from survivor lists (scores not stored)
+    ("random", 1, 1024, 20000, 2048, "normal"),
+    ("batch2_k1000", 2, 512, 30000, 1000, "normal"),
+    # the sampled key tiles (every 16th) score 8x higher: every row's list
+    # misses tokens, every query tile takes the materialised path
+    ("sample_misses", 1, 1024, 20000, 2048, "boost_sampled"),
+    # zero queries in every third query tile: all-tied rows overflow their
+    # lists; only those tiles take the materialised path
+    ("some_tiles_fall_back", 1, 1024, 20000, 2048, "zero_some_tiles"),
+    # integer scores: large tie groups at the threshold
+    ("integer_ties", 1, 640, 17000, 2048, "integers"),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_SEL, ids=[c[0] for c in STREAM_SEL])
+def test_stream_selection_equals_materialised(case):
+    """The whole layer's streamed selection (sampled scores, survivor
+    lists, exact selection, materialised path for undecided query tiles)
+    against the op-level indexer and top-k on the same inputs: identical
+    index lists and masks (both are exact selections of the same float32
+    scores; the op-level pair is checked against the oracle elsewhere)."""
+    name, B, T, q_pos0, top_k, recipe = case
+    n_kv = q_pos0 + T
+    wl = Workload(name=name, dtype="bf16", batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, idx_heads=32, idx_dim=128,
+                  top_k=top_k, heads=4, kv_heads=4, head_dim=64, seed=zlib.crc32(name.encode()) % 1000,
+                  integer_indexer=recipe == "integers", qidx_std=1 / math.sqrt(128), kidx_std=1.0,
+                  w_std=1 / math.sqrt(32))
+    g = make_inputs(wl, DEV)
+    if recipe == "boost_sampled":
+        tok = torch.arange(n_kv, device=DEV)
+        g["kidx"][:, (tok // 64) % 16 == 0] *= 8
+    if recipe == "zero_some_tiles":
+        t = torch.arange(T, device=DEV)
+        g["qidx"][:, (t // 32) % 3 == 0] = 0
+    r = _forward(g, wl, top_k, q_pos0, n_kv, return_mask=True, stream_select=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=q_pos0, n_kv=n_kv)
+    m, idx = dsa.topk_mask(sc, q_pos0=q_pos0, n_kv=n_kv, top_k=top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(r["indices"], idx)
+    assert torch.equal(r["mask"], m)
+    if recipe == "zero_some_tiles":  # all-tied rows keep their first top_k tokens
+        want = torch.arange(top_k, dtype=torch.int32, device=DEV)
+        assert torch.equal(r["indices"][0, 0], want)
+
+
 @pytest.mark.parametrize("T,q_pos0,n_kv,H,Hkv,D,dt", [(130, 20, 200, 4, 2, 128, "bf16"),
                                                       (1, 700, 701, 8, 8, 64, "bf16"),
                                                       (6, 300, 306, 16, 4, 128, "bf16"),
