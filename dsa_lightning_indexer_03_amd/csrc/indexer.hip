@@ -139,24 +139,25 @@ constexpr int kIdxQT = kIdxWaves * QPW;      // 32 queries per query tile
 #endif
 constexpr int kIdxKT = DSA_IDX_KT;            // keys per key tile
 static_assert(kIdxKT % kIdxQT == 0, "query tile divides key tile");
+static_assert((kIdxKT & (kIdxKT - 1)) == 0 && (kIdxQT & (kIdxQT - 1)) == 0, "power-of-two tiles");
 
 static_assert(kIdxQT == kIdxQueryTile, "query tile size shared with the host");
 
 struct UnitMap {
-  int T, q_pos0, nqt, nfull, ktw;  // ktw: keys spanned by one unit's key tile (kIdxKT x stride)
+  int T, q_pos0, nqt, nfull;
+  int lk, lr;  // log2 of the keys one unit's key tile spans (kIdxKT x stride) and of that / query tile
   long long per_seq;
-  __device__ __host__ int ntk(int qt) const { return (q_pos0 + min(kIdxQT * qt + kIdxQT - 1, T - 1)) / ktw + 1; }
-  // sum over x < n of floor(x / R), R = ktw / query tile
+  __device__ __host__ int ntk(int qt) const { return ((q_pos0 + min(kIdxQT * qt + kIdxQT - 1, T - 1)) >> lk) + 1; }
+  // sum over x < n of floor(x / R), R = 2^lr = key tile span / query tile
   __device__ __host__ long long floor_sum(long long n) const {
-    const int R = ktw / kIdxQT;
-    const long long m = n / R;
-    return R * m * (m - 1) / 2 + (n - R * m) * m;
+    const long long m = n >> lr;
+    return ((m * (m - 1) / 2) << lr) + (n - (m << lr)) * m;
   }
   // units of query tiles 0..n-1. A full query tile qt has
-  // floor((A + QT qt) / ktw) + 1 key tiles, A = q_pos0 + QT - 1; with
-  // A = a0 ktw + rq QT + rr (rr < QT) that is a0 + 1 + floor((qt + rq) / R).
+  // floor((A + QT qt) / span) + 1 key tiles, A = q_pos0 + QT - 1; with
+  // A = a0 span + rq QT + rr (rr < QT) that is a0 + 1 + floor((qt + rq) / R).
   __device__ __host__ long long prefix(int n) const {
-    const int A = q_pos0 + kIdxQT - 1, a0 = A / ktw, rq = (A % ktw) / kIdxQT;
+    const int A = q_pos0 + kIdxQT - 1, a0 = A >> lk, rq = (A & ((1 << lk) - 1)) / kIdxQT;
     const long long k = min(n, nfull);
     long long s = k * (a0 + 1) + floor_sum(rq + k) - floor_sum(rq);
     if (n > nfull) s += ntk(nfull);
@@ -171,11 +172,14 @@ struct UnitMap {
   __device__ __host__ long long prefix_pos(int n) const {
     return prefix((n + 1) >> 1) + per_seq - prefix(nqt - (n >> 1));
   }
-  // stride > 1: only every stride-th key tile (a sample of the keys)
+  // stride > 1 (a power of two): only every stride-th key tile (a sample of the keys)
   __device__ __host__ void init(int T_, int q_pos0_, int stride = 1) {
     T = T_;
     q_pos0 = q_pos0_;
-    ktw = kIdxKT * (stride > 1 ? stride : 1);
+    lk = 0;
+    while ((1 << lk) < kIdxKT * (stride > 1 ? stride : 1)) ++lk;
+    lr = lk;
+    while ((1 << (lk - lr)) < kIdxQT) --lr;
     nqt = (T + kIdxQT - 1) / kIdxQT;
     nfull = T / kIdxQT;
     per_seq = prefix(nqt);
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
 // 0..ntk(qt)-1 only). One workgroup per query row.
 __global__ __launch_bounds__(256) void scores_upper_fill_kernel(IndexerParams a, UnitMap um) {
   const int row = blockIdx.x, t = row % a.T;
-  const int s_from = um.ntk(t / kIdxQT) * um.ktw;
+  const int s_from = um.ntk(t / kIdxQT) << um.lk;
   float* srow = a.scores + (size_t)row * a.Lpad;
   const float ninf = fneg_inf();
   for (int s4 = s_from + 4 * threadIdx.x; s4 < a.Lpad; s4 += 4 * 256)
