@@ -41,7 +41,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X fp32
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 HEADLINE = "prefill_bf16_L4096"
-SECONDARY = ["decode_bf16_B64_L32768", "longctx_bf16_L65536_chunk4096", "longctx_mqa_bf16_L65536_chunk4096"]
+SECONDARY = ["decode_bf16_B64_L32768", "longctx_bf16_L65536_chunk4096", "longctx_mqa_bf16_L65536_chunk4096",
+             "longctx_kvshared_bf16_L65536_chunk4096"]
 
 
 def log(msg):

@@ -1,6 +1,7 @@
 // Sparse attention over gathered kept keys when every head shares one K/V
 // row per token (kv_heads == 1; a key-only latent cache passes the same
-// buffer as K and V), bf16, head dim 128, prefill-shaped calls.
+// buffer as K and V, and its rows are then gathered once), bf16, head dim
+// 128, prefill-shaped calls.
 //
 // The selection is shared by all heads of a query [aiaulis paras 2-4; devotd
 // section 2], so with one K/V row per token the kept rows serve every head:
@@ -37,7 +38,9 @@ __device__ __forceinline__ void dma16(const void* src, unsigned char* lds_wave_b
 
 constexpr int kMqaWaves = 4;  // query rows per workgroup
 
-template <int HB>  // heads = 16 HB
+// SHARED: K and V are one buffer (a key-only cache): each kept row is
+// gathered once, into the LDS tile, and the K operand is read back from it.
+template <int HB, bool SHARED>  // heads = 16 HB
 __global__ __launch_bounds__(64 * kMqaWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_mqa_bf16_kernel(GatherParams a) {
   constexpr int H = 16 * HB;
@@ -90,13 +93,23 @@ void attn_mqa_bf16_kernel(GatherParams a) {
       const int tr_ = __shfl(tok, r, 64);
       dma16(vbase + (size_t)tr_ * kD + (((lane & 15) ^ swz(r)) << 3), vl + i * 1024);
     }
-    // K fragments: key 16 kb + c.
+    // K fragments: key 16 kb + c (from the LDS tile when K is V: the rows
+    // landed once this wave's loads are done; no other wave writes it).
     bf16x8 kf[4][kKS];
+    if constexpr (SHARED) {
+      __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int tk = __shfl(tok, 16 * kb + c, 64);
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int kk = 0; kk < kKS; ++kk) kf[kb][kk] = load_frag<bf16>(kbase + (size_t)tk * kD + 32 * kk + 8 * g);
+        for (int kk = 0; kk < kKS; ++kk)
+          kf[kb][kk] = *reinterpret_cast<const bf16x8*>(vl + tile_off(16 * kb + c, 4 * kk + g));
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int tk = __shfl(tok, 16 * kb + c, 64);
+#pragma unroll
+        for (int kk = 0; kk < kKS; ++kk) kf[kb][kk] = load_frag<bf16>(kbase + (size_t)tk * kD + 32 * kk + 8 * g);
+      }
     }
 
     // S^T = K Q^T: lane (c, g) holds keys 16 kb + 4 g + r of head 16 hb + c.
@@ -208,10 +221,14 @@ hipError_t launch_attn_mqa_bf16(const GatherParams& p, hipStream_t st) {
   const long long rows = (long long)p.B * p.T;
   const long long nblocks = (rows + kMqaWaves - 1) / kMqaWaves;
   if (nblocks > 0x7fffffffll || !attn_mqa_bf16_supported(p.H, p.Hkv, kD)) return hipErrorInvalidValue;
-  if (p.H == 16)
-    hipLaunchKernelGGL((attn_mqa_bf16_kernel<1>), dim3((unsigned)nblocks), dim3(64 * kMqaWaves), 0, st, p);
-  else
-    hipLaunchKernelGGL((attn_mqa_bf16_kernel<2>), dim3((unsigned)nblocks), dim3(64 * kMqaWaves), 0, st, p);
+  const dim3 grid((unsigned)nblocks), block(64 * kMqaWaves);
+  if (p.k == p.v) {
+    if (p.H == 16) hipLaunchKernelGGL((attn_mqa_bf16_kernel<1, true>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((attn_mqa_bf16_kernel<2, true>), grid, block, 0, st, p);
+  } else {
+    if (p.H == 16) hipLaunchKernelGGL((attn_mqa_bf16_kernel<1, false>), grid, block, 0, st, p);
+    else hipLaunchKernelGGL((attn_mqa_bf16_kernel<2, false>), grid, block, 0, st, p);
+  }
   return hipGetLastError();
 }
 

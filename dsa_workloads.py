@@ -45,6 +45,7 @@ class Workload:
     kidx_std: float = 1.0
     w_std: float = 1.0
     qkv_std: float = 1.0
+    shared_kv: bool = False  # one buffer serves as K and V (kv_heads == 1: a key-only cache)
     description: str = ""
 
     @property
@@ -120,7 +121,15 @@ WORKLOADS = {
             idx_heads=32, idx_dim=128, top_k=2048, heads=32, kv_heads=1, head_dim=128,
             seed=6, chunks=16, qidx_std=_ws(128), kidx_std=_ws(128), w_std=_ws(32),
             description="long-context prefill as above with one K/V row per token "
-                        "shared by all 32 heads (the key-only cache reading)",
+                        "shared by all 32 heads (separate K and V rows)",
+        ),
+        Workload(
+            name="longctx_kvshared_bf16_L65536_chunk4096",
+            dtype="bf16", batch=1, n_q=65536, q_pos0=0, n_kv=65536,
+            idx_heads=32, idx_dim=128, top_k=2048, heads=32, kv_heads=1, head_dim=128,
+            seed=7, chunks=16, qidx_std=_ws(128), kidx_std=_ws(128), w_std=_ws(32), shared_kv=True,
+            description="long-context prefill with the key-only cache: one row per token "
+                        "serves as K and V for all 32 heads",
         ),
     ]
 }
@@ -163,7 +172,9 @@ def make_inputs(wl: Workload, device="cpu", kv_capacity=None):
     q = _normal((B, T, H, D), wl.qkv_std, dt, gen, dev)
     k = torch.zeros((B, cap, HKV, D), dtype=dt, device=dev)
     v = torch.zeros((B, cap, HKV, D), dtype=dt, device=dev)
-    for cache in (k, v):
+    if wl.shared_kv:  # one buffer, drawn once
+        v = k
+    for cache in (k,) if wl.shared_kv else (k, v):
         for b in range(B):
             cache[b, :L] = _normal((L, HKV, D), wl.qkv_std, dt, gen, dev)
     return {"qidx": qidx, "w": w, "kidx": kidx, "q": q, "k": k, "v": v}

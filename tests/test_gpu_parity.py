@@ -146,8 +146,17 @@ def test_decode_bf16_B64_L32768_all_rows():
     _say(f"stats {total}")
 
 
-def test_longctx_bf16_L65536_chunked_sampled_rows():
-    wl = WORKLOADS["longctx_bf16_L65536_chunk4096"]
+LONGCTX = ["longctx_bf16_L65536_chunk4096", "longctx_mqa_bf16_L65536_chunk4096",
+           "longctx_kvshared_bf16_L65536_chunk4096"]
+
+
+@pytest.mark.parametrize("name", LONGCTX)
+def test_longctx_L65536_chunked_sampled_rows(name):
+    """All 16 chunk calls at full size; 512 seeded rows (the first and last
+    of every chunk among them) against the oracle. The kv_heads == 1
+    workloads attend over the top-k index list; the key-only one passes one
+    buffer as K and V."""
+    wl = WORKLOADS[name]
     g = make_inputs(wl, DEV)
     C = wl.chunk_len
     out = torch.empty_like(g["q"])
@@ -180,6 +189,33 @@ def test_longctx_bf16_L65536_chunked_sampled_rows():
 
 
 # ------------------------------------------------------------------ edge cases
+
+SHARED_KV = [
+    # one buffer as K and V (a key-only cache): the kept-list attention
+    # gathers each kept row once
+    ("kvshared_ragged", "bf16", 2, 130, 37, 167, 170, 32, 128, 50, 32, 1, 128, False),
+    ("kvshared_multi_tile_h16", "bf16", 1, 200, 500, 700, 700, 32, 128, 300, 16, 1, 128, False),
+    ("kvshared_ties", "bf16", 1, 300, 0, 300, 300, 32, 128, 40, 32, 1, 128, True),
+]
+
+
+@pytest.mark.parametrize("edge", SHARED_KV, ids=[e[0] for e in SHARED_KV])
+def test_shared_kv_cache(edge):
+    wl, cap = _edge_wl(edge)
+    cpu = _edge_inputs(wl, cap)
+    cpu["v"] = cpu["k"]
+    g = _to(cpu, DEV)
+    g["v"] = g["k"]
+    res = _forward(g, wl, wl.top_k, wl.q_pos0, wl.n_kv, return_lse=True, return_mask=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=wl.q_pos0, n_kv=wl.n_kv)
+    # the op-level attention (mask -> list compaction) on the same buffer
+    alone = dsa.sparse_attention(g["q"], g["k"], g["v"], res["mask"], q_pos0=wl.q_pos0, n_kv=wl.n_kv,
+                                 scale=wl.scale)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        _check_sequence(wl, cpu, res, sc, b, range(wl.n_q), integer=wl.integer_indexer)
+    assert torch.equal(alone, res["out"])
+
 
 EDGE = [
     # name, dtype, B, T, q_pos0, n_kv, cap, HI, DI, k, H, Hkv, D, integer
