@@ -12,9 +12,12 @@ namespace {
 
 template <int NW, int EPT_R, int EPT_L>
 __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
-  if (a.row_flag && a.row_flag[(size_t)blockIdx.y * a.T + blockIdx.x] == 0u) return;
+  // last rows first: they have the most candidates (keep-all rows, which
+  // only write, fill in behind them)
+  const int t = a.T - 1 - (int)blockIdx.x;
+  if (a.row_flag && a.row_flag[(size_t)blockIdx.y * a.T + t] == 0u) return;
   __shared__ TopkShared<NW, EPT_L> sh;
-  topk_select_row<NW, EPT_R, EPT_L>(a, blockIdx.x, blockIdx.y, sh);
+  topk_select_row<NW, EPT_R, EPT_L>(a, t, blockIdx.y, sh);
 }
 
 
@@ -132,9 +135,9 @@ __device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t ran
 }
 
 __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) void topk_long_kernel(TopkParams a) {
-  if (a.row_flag && a.row_flag[(size_t)blockIdx.y * a.T + blockIdx.x] == 0u) return;
+  const int t = a.T - 1 - (int)blockIdx.x, b = blockIdx.y;  // longest rows first
+  if (a.row_flag && a.row_flag[(size_t)b * a.T + t] == 0u) return;
   __shared__ TopkLongShared sh;
-  const int t = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int q_pos0, n_kv;
   seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
