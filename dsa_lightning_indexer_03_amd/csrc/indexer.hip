@@ -355,6 +355,36 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
 
   int b, qp, kt;
   um.decode(u0, b, qp, kt);
+  QueryFrags<T, DI, QPW> f;
+  int cur_b = -1, cur_qt = -1;
+  int t_wave = 0, p_wave_last = -1, p_mine = 0;
+  float* srow = nullptr;  // this lane's score row, or nullptr when its query is past T
+  // scores of the previous unit, stored one unit late
+  float pend[NSUB];
+  float* pend_row = nullptr;
+  int pend_s0 = 0, pend_c0 = 0, pend_p = 0;
+  // streaming selection: this lane's row (or -1) and its survivor threshold
+  int row_mine = -1, pend_rowid = -1;
+  uint32_t guess_mine = 0, pend_guess = 0;
+  // the queries of query tile qt of sequence b: this wave's q fragments,
+  // head weights and output row
+  auto switch_tile = [&](int b, int qt) {
+    cur_b = b;
+    cur_qt = qt;
+    t_wave = qt * kIdxQT + wave * QPW;
+    const int nq = max(0, min(QPW, a.T - t_wave));
+    p_wave_last = a.q_pos0 + t_wave + nq - 1;
+    load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
+    const int t_mine = t_wave + jl;
+    p_mine = a.q_pos0 + t_mine;
+    srow = t_mine < a.T && !STREAM ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
+    if constexpr (STREAM) {
+      row_mine = t_mine < a.T ? b * a.T + t_mine : -1;
+      guess_mine = row_mine >= 0 ? a.guess[row_mine] : 0u;
+    }
+  };
+  // the first query tile's fragments travel with the prologue's key tiles
+  switch_tile(b, um.qt_at(qp));
   // Prologue: tiles of units u0 .. u0+S-2 (clamped to the range's last unit).
   int pb = b, ppos = qp, pkt = kt;  // prefetch cursor: the unit whose tile was loaded last
   long long pu = u0;
@@ -368,17 +398,6 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     dload(pb, pkt, i);
   }
 
-  QueryFrags<T, DI, QPW> f;
-  int cur_b = -1, cur_qt = -1;
-  int t_wave = 0, p_wave_last = -1, p_mine = 0;
-  float* srow = nullptr;  // this lane's score row, or nullptr when its query is past T
-  // scores of the previous unit, stored one unit late
-  float pend[NSUB];
-  float* pend_row = nullptr;
-  int pend_s0 = 0, pend_c0 = 0, pend_p = 0;
-  // streaming selection: this lane's row (or -1) and its survivor threshold
-  int row_mine = -1, pend_rowid = -1;
-  uint32_t guess_mine = 0, pend_guess = 0;
   auto flush = [&]() {
     if constexpr (STREAM) {
       // survivors (key prefix reaching the row's guess) appended to the row's
@@ -431,21 +450,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   int slot = 0;
   for (long long u = u0; u < u1; ++u) {
     const int qt = um.qt_at(qp);
-    if (b != cur_b || qt != cur_qt) {
-      cur_b = b;
-      cur_qt = qt;
-      t_wave = qt * kIdxQT + wave * QPW;
-      const int nq = max(0, min(QPW, a.T - t_wave));
-      p_wave_last = a.q_pos0 + t_wave + nq - 1;
-      load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
-      const int t_mine = t_wave + jl;
-      p_mine = a.q_pos0 + t_mine;
-      srow = t_mine < a.T && !STREAM ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
-      if constexpr (STREAM) {
-        row_mine = t_mine < a.T ? b * a.T + t_mine : -1;
-        guess_mine = row_mine >= 0 ? a.guess[row_mine] : 0u;
-      }
-    }
+    if (b != cur_b || qt != cur_qt) switch_tile(b, qt);
     // stores of unit u-1, then the tile of unit u+S-1 (or the range's last
     // one again) into the slot read at unit u-1: the newest S-2 tile loads
     // are then the last operations issued when tile u+1 is waited for
