@@ -72,6 +72,8 @@ def parse():
                          "beside the materialised one ('' for none)")
     ap.add_argument("--front-end-steps", type=int, default=20,
                     help="calls timed per indexer front-end workload (0 = skip)")
+    ap.add_argument("--cold-reps", type=int, default=5,
+                    help="steps timed after a 512 MiB cache-evicting write each (median reported; 0 = skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget of the oracle timing on the host (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -142,7 +144,7 @@ def op_work(wl, q_pos0, n_q, n_kv):
 
 # ----------------------------------------------------------------------------- GPU timing
 
-def run_gpu(wl, steps, warmup, torch, dsa, make_inputs):
+def run_gpu(wl, steps, warmup, torch, dsa, make_inputs, cold_reps=5):
     dev = torch.device("cuda:0")
     log(f"[bench] {wl.name}: drawing inputs on the GPU")
     g = make_inputs(wl, dev)
@@ -182,11 +184,31 @@ def run_gpu(wl, steps, warmup, torch, dsa, make_inputs):
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / steps
 
+    # Cold steps: before each, a 512 MiB scratch write (twice the last-level
+    # cache) on the same stream evicts the caches; HIP events bracket the step.
+    stream = torch.cuda.current_stream(dev)
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if cold_reps > 0 else None
+    cold_ms = []
+    for r in range(cold_reps):
+        scratch.fill_(r + 1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms.append(e0.elapsed_time(e1))
+    del scratch
+    cold = None
+    if cold_ms:
+        cold_ms.sort()
+        med = cold_ms[len(cold_ms) // 2]
+        cold = {"ms_per_step": round(med, 4), "value": wl.batch * wl.n_q / (med * 1e-3), "reps": len(cold_ms),
+                "flush": "512 MiB scratch write before each step"}
+
     # Per-op times: the same calls through the op-level entry points, HIP
     # events on the stream they are launched on. Every rep is enqueued before
     # any event is read, so the GPU runs the ops back to back and the event
     # pairs measure device time, not host launch gaps.
-    stream = torch.cuda.current_stream(dev)
     Lmax = (big[2] + 63) // 64 * 64
     scores = torch.empty((B, big[1], Lmax), dtype=torch.float32, device=dev)
     mask = torch.empty((B, big[1], Lmax // 32), dtype=torch.int32, device=dev)
@@ -244,6 +266,7 @@ def run_gpu(wl, steps, warmup, torch, dsa, make_inputs):
         "kernels": kernels,
         "dominant": dominant,
         "calls_per_step": len(calls),
+        "cold": cold,
     }
 
 
@@ -472,16 +495,16 @@ def main():
     dsa.lib()  # fails loudly if libdsa.so is missing
 
     wl = WORKLOADS[args.workload]
-    head = run_gpu(wl, args.steps, args.warmup, torch, dsa, make_inputs)
+    head = run_gpu(wl, args.steps, args.warmup, torch, dsa, make_inputs, args.cold_reps)
     log(f"[bench] {wl.name}: {head['ms_per_step']:.3f} ms/step, {head['value']:.4g} queries/s")
     secondary = []
     for name in [s for s in args.secondary.split(",") if s and s != args.workload]:
         steps2 = args.secondary_steps or secondary_steps_for(WORKLOADS[name])
-        r = run_gpu(WORKLOADS[name], steps2, steps2, torch, dsa, make_inputs)
+        r = run_gpu(WORKLOADS[name], steps2, steps2, torch, dsa, make_inputs, args.cold_reps)
         log(f"[bench] {name}: {r['ms_per_step']:.3f} ms/step, {r['value']:.4g} queries/s")
         secondary.append({
             "workload": name, "value": r["value"], "unit": "queries/s",
-            "ms_per_step": round(r["ms_per_step"], 4), "steps": steps2, "warmup": steps2,
+            "ms_per_step": round(r["ms_per_step"], 4), "steps": steps2, "warmup": steps2, "cold": r["cold"],
             "roofline": _roofline(r["dominant"], name), "kernels": r["kernels"],
         })
     front_end = []
@@ -536,6 +559,7 @@ def main():
             "tokens_per_s": head["value"],
         },
         "roofline": _roofline(head["dominant"], wl.name),
+        "cold": head["cold"],
         "cpu_baseline": cpu,
         "kernels": head["kernels"],
         "secondary": secondary,
