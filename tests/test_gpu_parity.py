@@ -269,6 +269,54 @@ def test_edge_cases(edge):
         assert np.all(np.isneginf(to_np(sc[b])[:, wl.n_kv :]))
 
 
+def _random_configs(n, seed):
+    """Seeded random layer configurations within the supported set: dtype,
+    indexer width, grouped or one-row-per-token K/V, decode- and
+    prefill-shaped calls, ragged offsets and capacities, integer ties, top_k
+    from 1 to past the context."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ("decode", "prefill", "mqa")[i % 3]
+        dt = "bf16" if kind == "mqa" or rng.random() < 0.6 else "fp32"
+        DI = int(rng.choice([32, 64, 128] if dt == "bf16" else [32, 64]))
+        HI = int(rng.integers(1, 33))
+        if kind == "mqa":
+            D, Hkv, H = 128, 1, int(rng.choice([16, 32]))
+        else:
+            D = int(rng.choice([64, 128]))
+            Hkv = int(rng.choice([1, 2, 4, 8]))
+            H = Hkv * int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 4))
+        T = int(rng.integers(1, 9)) if kind == "decode" else int(rng.integers(9, 200))
+        p0 = int(rng.integers(0, 1200))
+        nkv = p0 + T + int(rng.integers(0, 50))
+        cap = nkv + int(rng.integers(0, 20))
+        k = int(rng.choice([1, int(rng.integers(2, 64)), int(rng.integers(64, 700)), nkv + 5]))
+        integer = dt == "bf16" and rng.random() < 0.25
+        out.append((f"rand{i}_{kind}_{dt}", dt, B, T, p0, nkv, cap, HI, DI, k, H, Hkv, D, integer))
+    return out
+
+
+RANDOM = _random_configs(48, 2026)
+
+
+@pytest.mark.parametrize("cfg", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_configurations(cfg):
+    """Every query row of each configuration against the oracle (scores
+    within their bound, selections exact up to near-ties, outputs and
+    log-sum-exp within tolerance), and -inf scores past n_kv."""
+    wl, cap = _edge_wl(cfg)
+    cpu = _edge_inputs(wl, cap)
+    g = _to(cpu, DEV)
+    res = _forward(g, wl, wl.top_k, wl.q_pos0, wl.n_kv, return_lse=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=wl.q_pos0, n_kv=wl.n_kv)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        _check_sequence(wl, cpu, res, sc, b, range(wl.n_q), integer=wl.integer_indexer)
+        assert np.all(np.isneginf(to_np(sc[b])[:, wl.n_kv :]))
+
+
 @pytest.mark.parametrize("n_kv,T,top_k", [(300, 300, 37), (3500, 50, 2047), (5000, 40, 1000), (12000, 5, 2048),
                                           (20000, 6, 2048),
                                           (65536, 3, 2048), (65536, 2, 65000)])
