@@ -43,7 +43,24 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def _random_cases(n, seed):
+    """Seeded random calls: decode- and prefill-shaped, ragged offsets and
+    capacities, 1 to 32 heads, top_k below and past the context, integer
+    inputs now and then."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1, 9)) if i % 2 == 0 else int(rng.integers(9, 300))
+        p0 = int(rng.integers(0, 1500))
+        nkv = p0 + T + int(rng.integers(0, 40))
+        k = int(rng.choice([int(rng.integers(1, 100)), int(rng.integers(100, 800)), nkv + 3]))
+        out.append((f"rand{i}", int(rng.integers(1, 4)), T, p0, nkv, nkv + int(rng.integers(0, 20)),
+                    int(rng.integers(1, 33)), k, bool(rng.random() < 0.25)))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + _random_cases(12, 2028),
+                         ids=[c[0] for c in CASES] + [c[0] for c in _random_cases(12, 2028)])
 def test_fp8_indexer_parity(case):
     name, B, T, p0, nkv, cap, HI, k, integer = case
     full = Workload(name=name, dtype="bf16", batch=B, n_q=p0 + T, q_pos0=0, n_kv=nkv, idx_heads=HI, idx_dim=128,

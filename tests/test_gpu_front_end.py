@@ -106,3 +106,27 @@ def test_front_end_edge_cases(e):
     name, B, T, p0, cap, hid, r, HI, DI = e
     wl = FrontEndWorkload(name, B, T, p0, cap, hid, r, HI, DI, seed=sum(map(ord, name)) % 997)
     _run_and_check(wl)
+
+
+def _random_front_end(n, seed):
+    """Seeded random shapes: decode-sized to 1200 tokens, ragged offsets and
+    capacities, widths from 64 to 2560 (deep K takes the split path)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.choice([int(rng.integers(1, 9)), int(rng.integers(9, 200)), int(rng.integers(200, 1200))]))
+        p0 = int(rng.integers(0, 100))
+        out.append((f"rand{i}", int(rng.integers(1, 4)), T, p0, p0 + T + int(rng.integers(0, 20)),
+                    64 * int(rng.integers(1, 41)), 64 * int(rng.integers(1, 25)), int(rng.integers(1, 33)),
+                    int(rng.choice([32, 64, 128]))))
+    return out
+
+
+RANDOM = _random_front_end(16, 2027)
+
+
+@pytest.mark.parametrize("e", RANDOM, ids=[e[0] for e in RANDOM])
+def test_front_end_random_shapes(e):
+    name, B, T, p0, cap, hid, r, HI, DI = e
+    wl = FrontEndWorkload(name, B, T, p0, cap, hid, r, HI, DI, seed=sum(map(ord, name)) % 997)
+    _run_and_check(wl)
