@@ -62,7 +62,7 @@ typedef enum {
   DSA_OK = 0,
   DSA_ERR_NULL = 1,        /* a required pointer (or dims) is NULL          */
   DSA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range            */
-  DSA_ERR_UNSUPPORTED = 3, /* valid request this build has no kernel for    */
+  DSA_ERR_UNSUPPORTED = 3, /* valid request the library has no kernel for   */
   DSA_ERR_MISALIGNED = 4,  /* a pointer is not 16-byte aligned              */
   DSA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required       */
   DSA_ERR_HIP = 6          /* the HIP runtime rejected a launch             */
