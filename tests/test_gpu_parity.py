@@ -435,6 +435,23 @@ STREAM_SEL = [
 ]
 
 
+def _random_stream_cases(n, seed):
+    """Seeded random calls the streamed selection applies to (>= 512 rows,
+    longest row past 16384 tokens, top_k <= 2048)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        B = int(rng.integers(1, 3))
+        T = int(rng.integers(512 // B + 1, 1100))
+        p0 = int(rng.integers(16400 - T, 60000 - T))
+        k = int(rng.choice([1, int(rng.integers(2, 300)), int(rng.integers(300, 2049))]))
+        out.append((f"rand{i}", B, T, p0, k, "integers" if rng.random() < 0.25 else "normal"))
+    return out
+
+
+STREAM_SEL += _random_stream_cases(8, 2029)
+
+
 @pytest.mark.parametrize("case", STREAM_SEL, ids=[c[0] for c in STREAM_SEL])
 def test_stream_selection_equals_materialised(case):
     """The whole layer's streamed selection (sampled scores, survivor
