@@ -432,6 +432,8 @@ STREAM_SEL = [
     ("some_tiles_fall_back", 1, 1024, 20000, 2048, "zero_some_tiles"),
     # integer scores: large tie groups at the threshold
     ("integer_ties", 1, 640, 17000, 2048, "integers"),
+    # float32 layer (indexer dim 64)
+    ("fp32", 1, 600, 20000, 700, "normal_fp32"),
 ]
 
 
@@ -460,8 +462,11 @@ def test_stream_selection_equals_materialised(case):
     index lists and masks (both are exact selections of the same float32
     scores; the op-level pair is checked against the oracle elsewhere)."""
     name, B, T, q_pos0, top_k, recipe = case
+    fp32 = recipe.endswith("_fp32")
+    recipe = recipe.removesuffix("_fp32")
     n_kv = q_pos0 + T
-    wl = Workload(name=name, dtype="bf16", batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, idx_heads=32, idx_dim=128,
+    wl = Workload(name=name, dtype="fp32" if fp32 else "bf16", batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv,
+                  idx_heads=32, idx_dim=64 if fp32 else 128,
                   top_k=top_k, heads=4, kv_heads=4, head_dim=64, seed=zlib.crc32(name.encode()) % 1000,
                   integer_indexer=recipe == "integers", qidx_std=1 / math.sqrt(128), kidx_std=1.0,
                   w_std=1 / math.sqrt(32))
