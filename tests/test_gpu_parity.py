@@ -434,6 +434,9 @@ STREAM_SEL = [
     ("integer_ties", 1, 640, 17000, 2048, "integers"),
     # float32 layer (indexer dim 64)
     ("fp32", 1, 600, 20000, 700, "normal_fp32"),
+    # rows from 1 to 16800 tokens in one call: keep-all rows, rows whose every
+    # token fits the list (no guess), sampled rows
+    ("mixed_lengths", 1, 16800, 0, 2048, "normal"),
 ]
 
 
