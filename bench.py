@@ -42,7 +42,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 HEADLINE = "prefill_bf16_L4096"
 SECONDARY = ["decode_bf16_B64_L32768", "longctx_bf16_L65536_chunk4096", "longctx_mqa_bf16_L65536_chunk4096",
-             "longctx_kvshared_bf16_L65536_chunk4096"]
+             "longctx_kvshared_bf16_L65536_chunk4096", "tiny_fp32_L256", "equiv_bf16_L1536_k2048",
+             "ties_bf16_L1536_k512"]
 
 
 def log(msg):
@@ -273,9 +274,10 @@ def run_gpu(wl, steps, warmup, torch, dsa, make_inputs, cold_reps=5):
 def secondary_steps_for(wl):
     """Steps (and as many warmup steps) that fill about 100 ms for a
     secondary workload, from its algorithmic work at a nominal rate:
-    chunked long-context steps take tens of ms, a decode step half of one."""
-    est_ms = 25.0 if wl.chunks > 1 else 0.5
-    return int(min(200, max(3, round(100.0 / est_ms))))
+    chunked long-context steps take tens of ms, a decode step half of one,
+    the small (<= 2048-token) configurations tens of microseconds."""
+    est_ms = 25.0 if wl.chunks > 1 else (0.05 if wl.n_kv <= 2048 else 0.5)
+    return int(min(2000, max(3, round(100.0 / est_ms))))
 
 
 def front_end_work(fw):
