@@ -206,6 +206,24 @@ def test_selection_invariant_under_power_of_two_scaling():
         assert np.array_equal(select_topk(row, 299, 50), select_topk(row * np.float32(2.0**j), 299, 50))
 
 
+def test_selection_decided_on_float32_rounded_scores():
+    # Scores 1 and 1 + 2^-30 differ in float64 but not in float32, whose
+    # significand has 24 bits: decided in float32 the two tie and the lower
+    # index is kept. Catches a selection taken on the float64 scores, and a
+    # rounding that keeps the sign of a zero score.
+    qidx = np.ones((2, 1, 1))
+    w = np.ones((2, 1))
+    kidx = np.array([[1.0], [1.0 + 2.0**-30]])
+    zeros = np.zeros((2, 1, 1))
+    r = dsa_rows(qidx, w, kidx, zeros, zeros, zeros, q_pos0=0, top_k=1, scale=1.0, rows=[1])
+    assert r["scores64"][0][1] > r["scores64"][0][0]
+    assert list(r["sel"][0]) == [0]
+    s = round_scores_fp32(np.array([1.0 + 2.0**-30, -0.0]))
+    assert s.dtype == np.float32
+    assert s[0] == np.float32(1.0)
+    assert s[1] == 0.0 and not np.signbit(s[1])
+
+
 def test_padded_indices_and_mask_words():
     g = _load("mask_words.json")
     for c in g["cases"]:

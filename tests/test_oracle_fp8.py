@@ -46,10 +46,13 @@ def test_random_and_tie_values_match_torch():
 
 @pytest.mark.parametrize("x,want", [(0.1, 0.1015625), (1.0625, 1.0), (1.1875, 1.25), (2.0 ** -10, 0.0),
                                     (3 * 2.0 ** -10, 2.0 ** -8), (447.0, 448.0), (460.0, 448.0),
+                                    (470.0, 448.0), (-500.0, -448.0), (1.0e6, 448.0),
                                     (-149.33, -144.0), (0.0, 0.0)])
 def test_worked_values(x, want):
     """From the definition: step 2^(e-3) for normal values, 2^-9 below 2^-6,
-    ties to the even mantissa, saturation at 448."""
+    ties to the even mantissa, saturation at 448 (460 is below the midpoint
+    464 between 448 and 480 and rounds to 448 anyway; 470, -500 and 1e6 reach
+    448 only by saturating)."""
     assert e4m3_round(np.float32(x)) == want
 
 
