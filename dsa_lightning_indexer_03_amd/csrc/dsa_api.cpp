@@ -605,7 +605,20 @@ static dsa_status forward_impl(const dsa_dims* dims, const void* qidx, const flo
   if (stream_select && use_stream_select(d)) {
     DSA_TRY(run_stream_select(d, qidx, w, kidx, wsb, fw, m, idx, st));
   } else {
-    DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
+    // A query at position p with p + 1 <= top_k keeps every earlier token
+    // whatever the scores say, and the top-k writes its selection without
+    // reading a score, so its row is not scored. With one sequence these are
+    // the call's first rows; the rest are scored as a call of their own.
+    const int skip = d.batch == 1 ? std::min(std::max(d.top_k - d.q_pos0, 0), d.n_q) : 0;
+    if (skip < d.n_q) {
+      dsa_dims ds = d;
+      ds.n_q = d.n_q - skip;
+      ds.q_pos0 = d.q_pos0 + skip;
+      const size_t esz = d.dtype == DSA_BF16 ? 2 : 4;
+      const void* qs = static_cast<const unsigned char*>(qidx) + (size_t)skip * d.idx_heads * d.idx_dim * esz;
+      DSA_TRY(run_scores(ds, qs, w + (size_t)skip * d.idx_heads, kidx, scores + (size_t)skip * lpad_of(d), false,
+                         st));
+    }
     DSA_TRY(run_topk(d, scores, m, idx, st));
   }
   DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather || mqa ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw,
