@@ -607,17 +607,28 @@ static dsa_status forward_impl(const dsa_dims* dims, const void* qidx, const flo
   } else {
     // A query at position p with p + 1 <= top_k keeps every earlier token
     // whatever the scores say, and the top-k writes its selection without
-    // reading a score, so its row is not scored. With one sequence these are
-    // the call's first rows; the rest are scored as a call of their own.
-    const int skip = d.batch == 1 ? std::min(std::max(d.top_k - d.q_pos0, 0), d.n_q) : 0;
-    if (skip < d.n_q) {
+    // reading a score, so its row is not scored. These are the first `skip`
+    // rows of every sequence. When they are all the rows nothing is scored;
+    // otherwise the rest of each sequence is scored as a call of its own
+    // (one call per sequence, for batches of up to kCutMaxBatch sequences;
+    // larger batches score every row in one call).
+    constexpr int kCutMaxBatch = 8;
+    const int skip = std::min(std::max(d.top_k - d.q_pos0, 0), d.n_q);
+    if (skip == 0 || (skip < d.n_q && d.batch > kCutMaxBatch)) {
+      DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
+    } else if (skip < d.n_q) {
       dsa_dims ds = d;
+      ds.batch = 1;
       ds.n_q = d.n_q - skip;
       ds.q_pos0 = d.q_pos0 + skip;
       const size_t esz = d.dtype == DSA_BF16 ? 2 : 4;
-      const void* qs = static_cast<const unsigned char*>(qidx) + (size_t)skip * d.idx_heads * d.idx_dim * esz;
-      DSA_TRY(run_scores(ds, qs, w + (size_t)skip * d.idx_heads, kidx, scores + (size_t)skip * lpad_of(d), false,
-                         st));
+      const size_t qrow = (size_t)d.idx_heads * d.idx_dim * esz;  // bytes per query row of qidx
+      for (int b = 0; b < d.batch; ++b) {
+        const size_t row0 = (size_t)b * d.n_q + skip;  // first scored row of sequence b
+        const void* qs = static_cast<const unsigned char*>(qidx) + row0 * qrow;
+        const void* ks = static_cast<const unsigned char*>(kidx) + (size_t)b * d.kv_capacity * d.idx_dim * esz;
+        DSA_TRY(run_scores(ds, qs, w + row0 * d.idx_heads, ks, scores + row0 * lpad_of(d), false, st));
+      }
     }
     DSA_TRY(run_topk(d, scores, m, idx, st));
   }

@@ -143,11 +143,11 @@ dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void*
  * with the scores kept in the workspace [aiaulis paras 2-4; devotd sections
  * 1-2]. `indices`, `mask` and `lse` are optional outputs (NULL = not
  * written; the mask then lives in the workspace). Attention paths that
- * gather kept rows read top-k's index list directly. With one sequence,
- * queries at positions below top_k keep every earlier token and are not
- * scored (the workspace holds no scores for them; no output depends on
- * them). Needs dsa_workspace_size(dims, DSA_OP_FORWARD) bytes of
- * workspace. */
+ * gather kept rows read top-k's index list directly. Queries at positions
+ * below top_k keep every earlier token and are not scored (the workspace
+ * holds no scores for them; no output depends on them), except in batches
+ * of more than 8 sequences that also have rows to score. Needs
+ * dsa_workspace_size(dims, DSA_OP_FORWARD) bytes of workspace. */
 dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w,
                        const void* kidx, const void* q, const void* k_cache,
                        const void* v_cache, void* out, float* lse, int32_t* indices,
