@@ -470,13 +470,37 @@ def _random_stream_cases(n, seed):
 STREAM_SEL += _random_stream_cases(8, 2029)
 
 
+def _stream_rows(name, B, T, q_pos0, top_k, recipe):
+    """Rows of a streamed-selection case checked against the oracle, per
+    sequence: every row of the two cheapest cases; otherwise the first and
+    last rows, both rows at every 32-row query-tile edge of the first and
+    last tiles, rows of query tiles that fall back to the materialised path,
+    keep-all rows and rows whose every candidate fits the survivor list
+    (mixed lengths), and seeded random rows (96 per sequence, 128 for the
+    mixed-length call)."""
+    if name in ("fp32", "integer_ties"):
+        return list(range(T))
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + 17)
+    must = {0, 1, 31, 32, T - 33, T - 32, T - 2, T - 1}
+    if recipe == "zero_some_tiles":  # tiles 0, 3, 6, ... fall back
+        must |= {0, 2, 95, 96, 97, 191, 3 * 32 * (T // 96) - 1}
+    if name == "mixed_lengths":
+        must |= {top_k - 2, top_k - 1, top_k, 8190, 8191, 8192, 16383, 16384, 16385}
+    n = 128 if name == "mixed_lengths" else 96
+    rest = [int(r) for r in rng.permutation(T) if int(r) not in must]
+    rows = sorted(r for r in must if 0 <= r < T)
+    return sorted(rows + rest[: max(0, n - len(rows))])
+
+
 @pytest.mark.parametrize("case", STREAM_SEL, ids=[c[0] for c in STREAM_SEL])
-def test_stream_selection_equals_materialised(case):
-    """The whole layer's streamed selection (sampled scores, survivor
-    lists, exact selection, materialised path for undecided query tiles)
-    against the op-level indexer and top-k on the same inputs: identical
-    index lists and masks (both are exact selections of the same float32
-    scores; the op-level pair is checked against the oracle elsewhere)."""
+def test_stream_selection_against_oracle(case):
+    """dsa_forward_stream_select (sampled scores, survivor lists, exact
+    selection, materialised path for undecided query tiles) on long rows
+    [devotd section 2]: kept sets and outputs of the chosen rows against the
+    oracle (sets exact up to near-ties, bit-exact on integer inputs; outputs
+    and lse within tolerance); on every row, indices, mask, out and lse
+    bit-equal to dsa_forward on the same inputs, and indices and mask equal
+    to the op-level indexer + top-k."""
     name, B, T, q_pos0, top_k, recipe = case
     fp32 = recipe.endswith("_fp32")
     recipe = recipe.removesuffix("_fp32")
@@ -493,15 +517,24 @@ def test_stream_selection_equals_materialised(case):
     if recipe == "zero_some_tiles":
         t = torch.arange(T, device=DEV)
         g["qidx"][:, (t // 32) % 3 == 0] = 0
-    r = _forward(g, wl, top_k, q_pos0, n_kv, return_mask=True, stream_select=True)
+    r = _forward(g, wl, top_k, q_pos0, n_kv, return_mask=True, return_lse=True, stream_select=True)
+    r0 = _forward(g, wl, top_k, q_pos0, n_kv, return_mask=True, return_lse=True)
     sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=q_pos0, n_kv=n_kv)
     m, idx = dsa.topk_mask(sc, q_pos0=q_pos0, n_kv=n_kv, top_k=top_k)
     torch.cuda.synchronize()
     assert torch.equal(r["indices"], idx)
     assert torch.equal(r["mask"], m)
+    for key in ("indices", "mask", "out", "lse"):
+        assert torch.equal(r[key], r0[key]), f"{key} differs from dsa_forward"
     if recipe == "zero_some_tiles":  # all-tied rows keep their first top_k tokens
         want = torch.arange(top_k, dtype=torch.int32, device=DEV)
         assert torch.equal(r["indices"][0, 0], want)
+    rows = _stream_rows(name, B, T, q_pos0, top_k, recipe)
+    cpu = {k: v.cpu() for k, v in g.items()}
+    for b in range(B):
+        st = _check_sequence(wl, cpu, r, None, b, rows, integer=wl.integer_indexer)
+        _say(f"{name} seq {b}: {st}")
+        assert st["rows"] == len(rows)
 
 
 @pytest.mark.parametrize("T,q_pos0,n_kv,H,Hkv,D,dt", [(130, 20, 200, 4, 2, 128, "bf16"),
