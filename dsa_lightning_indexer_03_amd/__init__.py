@@ -8,7 +8,8 @@ step of the layer runs in the library's kernels. There is no fallback: if the
 library is missing or a tensor is not on the GPU, calls raise.
 
 Entry points (same names as the C ABI, without the prefix):
-  index_scores, topk_mask, sparse_attention, forward, forward_varlen,
+  index_scores, topk_mask, sparse_attention, forward (with stream_select /
+  noalloc: dsa_forward_stream_select / dsa_forward_noalloc), forward_varlen,
   indexer_project, quantize_fp8, quantize_keys_fp8, index_scores_fp8,
   workspace_size
 """
@@ -72,6 +73,8 @@ _SIGS = {
                                                  _P, _P, ctypes.c_size_t, _P]),
     "dsa_forward_varlen": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _P, ctypes.c_size_t, _P]),
+    "dsa_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           _P, _P]),
     "dsa_quantize_fp8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P, _P, _P]),
     "dsa_index_scores_fp8": (ctypes.c_int, [ctypes.POINTER(Dims), _P, _P, _P, _P, _P, _P]),
     "dsa_indexer_project": (ctypes.c_int, [ctypes.POINTER(ProjDims), _P, _P, _P, _P, _P, _P, _P, _P,
@@ -234,7 +237,7 @@ def sparse_attention(q, k, v, mask, *, q_pos0=0, n_kv=None, scale=None, lse=Fals
 
 def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
             return_indices=True, return_mask=False, return_lse=False, workspace=None, out=None,
-            indices=None, mask=None, lse=None, seq_lens=None, stream_select=False):
+            indices=None, mask=None, lse=None, seq_lens=None, stream_select=False, noalloc=False):
     """The whole DSA layer. Returns a dict with 'out' and the requested extras
     ('indices' [B, T, top_k] int32, 'mask' [B, T, Lpad/32] int32, 'lse').
     Passing `out`, `indices`, `mask`, `lse` or `workspace` tensors makes the
@@ -244,7 +247,11 @@ def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
     queries are its last T positions; `n_kv` (default: the caches' capacity)
     is the longest sequence and `q_pos0` is ignored. With `stream_select` the
     call goes to dsa_forward_stream_select (the same results; long rows take
-    their selection from survivor lists instead of stored scores)."""
+    their selection from survivor lists instead of stored scores). With
+    `noalloc` the call goes to dsa_forward_noalloc (the same results; the
+    workspace is the library's fixed device array, so no workspace tensor is
+    allocated; pass `out` and the wanted extras to allocate nothing here
+    either)."""
     _need_gpu(qidx, w, kidx, q, k, v, workspace, out, indices, mask, lse, seq_lens)
     B, T, HI, DI = qidx.shape
     H, D = q.shape[2], q.shape[3]
@@ -276,6 +283,13 @@ def forward(qidx, w, kidx, q, k, v, *, top_k, q_pos0=0, n_kv=None, scale=None,
             res[name] = torch.empty(shape, dtype=dt, device=dev)
     if stream_select and seq_lens is not None:
         raise ValueError("stream_select applies to prefill-shaped calls, not varlen decode batches")
+    if noalloc:
+        if stream_select or seq_lens is not None or workspace is not None:
+            raise ValueError("noalloc takes no workspace and applies to dsa_forward calls only")
+        _check(lib().dsa_forward_noalloc(ctypes.byref(d), _ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(res["out"]), _ptr(res.get("lse")),
+                                         _ptr(res.get("indices")), _ptr(res.get("mask")), _stream(q)))
+        return res
     ws, nbytes = _workspace(d, DSA_OP_FORWARD_STREAM if stream_select else DSA_OP_FORWARD, dev, workspace)
     tail = (_ptr(qidx), _ptr(w), _ptr(kidx), _ptr(q), _ptr(k), _ptr(v), _ptr(res["out"]),
             _ptr(res.get("lse")), _ptr(res.get("indices")), _ptr(res.get("mask")), _ptr(ws), nbytes,

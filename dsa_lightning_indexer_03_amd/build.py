@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "attn_prefill_bf16.hip", "attn_mqa_bf16.hip", "front_end.hip",
-           "fp8_quant.hip", "dsa_api.cpp"]
+           "fp8_quant.hip", "noalloc.hip", "dsa_api.cpp"]
 LIB_NAME = "libdsa.so"
 ARCH = "gfx950"
 

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <string>
 
+#include "dsa_internal.hpp"
 #include "dsa_kernels.hpp"
 
 namespace {
@@ -406,6 +407,81 @@ size_t proj_ws(const dsa_proj_dims& d) {
 
 }  // namespace
 
+static dsa_status forward_impl(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx, const void* q,
+                        const void* k_cache, const void* v_cache, void* out, float* lse, int32_t* indices,
+                        uint32_t* mask, void* ws, size_t ws_bytes, void* stream, bool stream_select,
+                        dsa::WorkspaceProvider provider = nullptr) {
+  DSA_TRY(check_dims(dims, true, true, true));
+  DSA_TRY(check_ptr(qidx, "qidx"));
+  DSA_TRY(check_ptr(w, "w"));
+  DSA_TRY(check_ptr(kidx, "kidx"));
+  DSA_TRY(check_ptr(q, "q"));
+  DSA_TRY(check_ptr(k_cache, "k_cache"));
+  DSA_TRY(check_ptr(v_cache, "v_cache"));
+  DSA_TRY(check_ptr(out, "out"));
+  DSA_TRY(check_ptr(lse, "lse", false));
+  DSA_TRY(check_ptr(indices, "indices", false));
+  DSA_TRY(check_ptr(mask, "mask", false));
+  const dsa_dims& d = *dims;
+  const FwdWs fw = fwd_ws(d, mask != nullptr, indices != nullptr, stream_select);
+  if (provider) DSA_TRY(provider(fw.total, &ws, &ws_bytes));
+  DSA_TRY(check_ptr(ws, "workspace"));
+  if (ws_bytes < fw.total) return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, fw.total);
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* wsb = (unsigned char*)ws;
+  float* scores = reinterpret_cast<float*>(wsb + fw.scores);
+  uint32_t* m = mask ? mask : reinterpret_cast<uint32_t*>(wsb + fw.mask);
+  const bool gather = use_gather(d);
+  const bool mqa = use_mqa_list(d);
+  int32_t* idx = indices ? indices : (gather || mqa ? reinterpret_cast<int32_t*>(wsb + fw.indices) : nullptr);
+  if (stream_select && use_stream_select(d)) {
+    DSA_TRY(run_stream_select(d, qidx, w, kidx, wsb, fw, m, idx, st));
+  } else {
+    // A query at position p with p + 1 <= top_k keeps every earlier token
+    // whatever the scores say, and the top-k writes its selection without
+    // reading a score, so its row is not scored. These are the first `skip`
+    // rows of every sequence. When they are all the rows nothing is scored;
+    // otherwise the rest of each sequence is scored as a call of its own
+    // (one call per sequence, for batches of up to kCutMaxBatch sequences;
+    // larger batches score every row in one call).
+    constexpr int kCutMaxBatch = 8;
+    const int skip = std::min(std::max(d.top_k - d.q_pos0, 0), d.n_q);
+    if (skip == 0 || (skip < d.n_q && d.batch > kCutMaxBatch)) {
+      DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
+    } else if (skip < d.n_q) {
+      dsa_dims ds = d;
+      ds.batch = 1;
+      ds.n_q = d.n_q - skip;
+      ds.q_pos0 = d.q_pos0 + skip;
+      const size_t esz = d.dtype == DSA_BF16 ? 2 : 4;
+      const size_t qrow = (size_t)d.idx_heads * d.idx_dim * esz;  // bytes per query row of qidx
+      for (int b = 0; b < d.batch; ++b) {
+        const size_t row0 = (size_t)b * d.n_q + skip;  // first scored row of sequence b
+        const void* qs = static_cast<const unsigned char*>(qidx) + row0 * qrow;
+        const void* ks = static_cast<const unsigned char*>(kidx) + (size_t)b * d.kv_capacity * d.idx_dim * esz;
+        DSA_TRY(run_scores(ds, qs, w + row0 * d.idx_heads, ks, scores + row0 * lpad_of(d), false, st));
+      }
+    }
+    DSA_TRY(run_topk(d, scores, m, idx, st));
+  }
+  DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather || mqa ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw,
+                        st));
+  return ok();
+}
+
+namespace dsa {
+
+dsa_status forward_with_provider(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
+                                 const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                 int32_t* indices, uint32_t* mask, WorkspaceProvider provider, void* stream) {
+  return forward_impl(dims, qidx, w, kidx, q, k_cache, v_cache, out, lse, indices, mask, nullptr, 0, stream, false,
+                      provider);
+}
+
+dsa_status set_error(dsa_status st, const char* msg) { return fail(st, "%s", msg); }
+
+}  // namespace dsa
+
 extern "C" {
 
 dsa_status dsa_indexer_project(const dsa_proj_dims* dims, const void* x, const void* q_lat, const void* w_qb,
@@ -574,66 +650,6 @@ dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void*
   }
   DSA_TRY(run_attention(*dims, q, k_cache, v_cache, mask, nullptr, out, lse, (unsigned char*)ws, aw,
                         (hipStream_t)stream));
-  return ok();
-}
-
-static dsa_status forward_impl(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx, const void* q,
-                        const void* k_cache, const void* v_cache, void* out, float* lse, int32_t* indices,
-                        uint32_t* mask, void* ws, size_t ws_bytes, void* stream, bool stream_select) {
-  DSA_TRY(check_dims(dims, true, true, true));
-  DSA_TRY(check_ptr(qidx, "qidx"));
-  DSA_TRY(check_ptr(w, "w"));
-  DSA_TRY(check_ptr(kidx, "kidx"));
-  DSA_TRY(check_ptr(q, "q"));
-  DSA_TRY(check_ptr(k_cache, "k_cache"));
-  DSA_TRY(check_ptr(v_cache, "v_cache"));
-  DSA_TRY(check_ptr(out, "out"));
-  DSA_TRY(check_ptr(lse, "lse", false));
-  DSA_TRY(check_ptr(indices, "indices", false));
-  DSA_TRY(check_ptr(mask, "mask", false));
-  const dsa_dims& d = *dims;
-  const FwdWs fw = fwd_ws(d, mask != nullptr, indices != nullptr, stream_select);
-  DSA_TRY(check_ptr(ws, "workspace"));
-  if (ws_bytes < fw.total) return fail(DSA_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, fw.total);
-  hipStream_t st = (hipStream_t)stream;
-  unsigned char* wsb = (unsigned char*)ws;
-  float* scores = reinterpret_cast<float*>(wsb + fw.scores);
-  uint32_t* m = mask ? mask : reinterpret_cast<uint32_t*>(wsb + fw.mask);
-  const bool gather = use_gather(d);
-  const bool mqa = use_mqa_list(d);
-  int32_t* idx = indices ? indices : (gather || mqa ? reinterpret_cast<int32_t*>(wsb + fw.indices) : nullptr);
-  if (stream_select && use_stream_select(d)) {
-    DSA_TRY(run_stream_select(d, qidx, w, kidx, wsb, fw, m, idx, st));
-  } else {
-    // A query at position p with p + 1 <= top_k keeps every earlier token
-    // whatever the scores say, and the top-k writes its selection without
-    // reading a score, so its row is not scored. These are the first `skip`
-    // rows of every sequence. When they are all the rows nothing is scored;
-    // otherwise the rest of each sequence is scored as a call of its own
-    // (one call per sequence, for batches of up to kCutMaxBatch sequences;
-    // larger batches score every row in one call).
-    constexpr int kCutMaxBatch = 8;
-    const int skip = std::min(std::max(d.top_k - d.q_pos0, 0), d.n_q);
-    if (skip == 0 || (skip < d.n_q && d.batch > kCutMaxBatch)) {
-      DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
-    } else if (skip < d.n_q) {
-      dsa_dims ds = d;
-      ds.batch = 1;
-      ds.n_q = d.n_q - skip;
-      ds.q_pos0 = d.q_pos0 + skip;
-      const size_t esz = d.dtype == DSA_BF16 ? 2 : 4;
-      const size_t qrow = (size_t)d.idx_heads * d.idx_dim * esz;  // bytes per query row of qidx
-      for (int b = 0; b < d.batch; ++b) {
-        const size_t row0 = (size_t)b * d.n_q + skip;  // first scored row of sequence b
-        const void* qs = static_cast<const unsigned char*>(qidx) + row0 * qrow;
-        const void* ks = static_cast<const unsigned char*>(kidx) + (size_t)b * d.kv_capacity * d.idx_dim * esz;
-        DSA_TRY(run_scores(ds, qs, w + row0 * d.idx_heads, ks, scores + row0 * lpad_of(d), false, st));
-      }
-    }
-    DSA_TRY(run_topk(d, scores, m, idx, st));
-  }
-  DSA_TRY(run_attention(d, q, k_cache, v_cache, m, gather || mqa ? idx : nullptr, out, lse, wsb + fw.attn, fw.aw,
-                        st));
   return ok();
 }
 

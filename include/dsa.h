@@ -198,6 +198,30 @@ dsa_status dsa_forward_stream_select(const dsa_dims* dims, const void* qidx, con
                                      const void* v_cache, void* out, float* lse, int32_t* indices,
                                      uint32_t* mask, void* ws, size_t ws_bytes, void* stream);
 
+/* dsa_forward without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. The workspace is a
+ * fixed device array of DSA_NOALLOC_SCRATCH_BYTES inside the library, one
+ * per GPU, held until the process ends; its device address is looked up once
+ * per device (on the first call with that device current) and nothing is
+ * allocated or freed, by the library or any routine it calls.
+ *  - Runs on the calling thread's current device; `stream` must belong to it.
+ *  - Calls whose dsa_forward workspace (dsa_workspace_size(dims,
+ *    DSA_OP_FORWARD), less the mask and index-list regions when `mask` /
+ *    `indices` are given) exceeds DSA_NOALLOC_SCRATCH_BYTES return
+ *    DSA_ERR_WORKSPACE and enqueue nothing. The decode batch of 64 sequences
+ *    x 32768 cached tokens (32 x 128 indexer and attention heads, top_k 2048)
+ *    needs about 25 MiB.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (concurrent streams, or threads) race and give undefined results;
+ *    serialise them. Results never depend on what an earlier call left in
+ *    the array.
+ * Every other argument, layout, result and error behaviour is dsa_forward's. */
+#define DSA_NOALLOC_SCRATCH_BYTES (32u * 1024u * 1024u)
+dsa_status dsa_forward_noalloc(const dsa_dims* dims, const void* qidx, const float* w, const void* kidx,
+                               const void* q, const void* k_cache, const void* v_cache, void* out,
+                               float* lse, int32_t* indices, uint32_t* mask, void* stream);
+
 /* fp8 reading of the indexer (a precision study: the pages keep the
  * indexer's tensors unquantised because top-k selection is sensitive to their
  * precision [aiaulis para 5; aiu "What happened"; devotd section 3]).

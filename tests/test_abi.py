@@ -103,6 +103,28 @@ def test_attention_and_forward_validation():
     assert "need" in _err()
 
 
+def test_forward_noalloc_validation():
+    """The allocation-free forward validates like dsa_forward and refuses
+    calls whose workspace exceeds its fixed device array, all on the host
+    before it looks the array up or enqueues anything."""
+    lib = dsa.lib()
+
+    def call(d, out=FAKE):
+        return lib.dsa_forward_noalloc(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, out, None, None, None,
+                                       None)
+
+    assert call(_dims(top_k=0)) == ERR_SHAPE
+    assert call(_dims(), out=None) == ERR_NULL
+    # 256 decode sequences of 32768 tokens: about 100 MiB of workspace
+    big = _dims(batch=256, n_q=1, q_pos0=32767, n_kv=32768, kv_capacity=32768, top_k=2048)
+    assert dsa.workspace_size(big, dsa.DSA_OP_FORWARD) > 32 << 20
+    assert call(big) == ERR_WORKSPACE
+    assert "scratch" in _err()
+    # the decode batch of 64 sequences x 32768 tokens fits
+    dec = _dims(batch=64, n_q=1, q_pos0=32767, n_kv=32768, kv_capacity=32768, top_k=2048)
+    assert dsa.workspace_size(dec, dsa.DSA_OP_FORWARD) <= 32 << 20
+
+
 def test_topk_validation():
     lib = dsa.lib()
     d = _dims(top_k=0)
