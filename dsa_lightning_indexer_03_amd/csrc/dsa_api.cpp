@@ -227,8 +227,11 @@ dsa::IndexerParams indexer_params(const dsa_dims& d, const void* qidx, const flo
 }
 
 dsa_status run_scores(const dsa_dims& d, const void* qidx, const float* w, const void* kidx, float* scores,
-                      bool write_upper, hipStream_t st, const int32_t* seq_len = nullptr) {
-  const dsa::IndexerParams p = indexer_params(d, qidx, w, kidx, scores, write_upper, seq_len);
+                      bool write_upper, hipStream_t st, const int32_t* seq_len = nullptr, int row0 = 0,
+                      int T_ld = 0) {
+  dsa::IndexerParams p = indexer_params(d, qidx, w, kidx, scores, write_upper, seq_len);
+  p.row0 = row0;
+  p.T_ld = T_ld;
   return hip_status(dsa::launch_indexer(p, d.dtype, d.idx_dim, st), "indexer launch", st);
 }
 
@@ -440,27 +443,17 @@ static dsa_status forward_impl(const dsa_dims* dims, const void* qidx, const flo
     // A query at position p with p + 1 <= top_k keeps every earlier token
     // whatever the scores say, and the top-k writes its selection without
     // reading a score, so its row is not scored. These are the first `skip`
-    // rows of every sequence. When they are all the rows nothing is scored;
-    // otherwise the rest of each sequence is scored as a call of its own
-    // (one call per sequence, for batches of up to kCutMaxBatch sequences;
-    // larger batches score every row in one call).
-    constexpr int kCutMaxBatch = 8;
+    // rows of every sequence: the indexer runs over the remaining rows of
+    // every sequence in one launch (row offset `skip` into each sequence's
+    // qidx, w and scores rows), and not at all when no row is left.
     const int skip = std::min(std::max(d.top_k - d.q_pos0, 0), d.n_q);
-    if (skip == 0 || (skip < d.n_q && d.batch > kCutMaxBatch)) {
+    if (skip == 0) {
       DSA_TRY(run_scores(d, qidx, w, kidx, scores, false, st));
     } else if (skip < d.n_q) {
       dsa_dims ds = d;
-      ds.batch = 1;
       ds.n_q = d.n_q - skip;
       ds.q_pos0 = d.q_pos0 + skip;
-      const size_t esz = d.dtype == DSA_BF16 ? 2 : 4;
-      const size_t qrow = (size_t)d.idx_heads * d.idx_dim * esz;  // bytes per query row of qidx
-      for (int b = 0; b < d.batch; ++b) {
-        const size_t row0 = (size_t)b * d.n_q + skip;  // first scored row of sequence b
-        const void* qs = static_cast<const unsigned char*>(qidx) + row0 * qrow;
-        const void* ks = static_cast<const unsigned char*>(kidx) + (size_t)b * d.kv_capacity * d.idx_dim * esz;
-        DSA_TRY(run_scores(ds, qs, w + row0 * d.idx_heads, ks, scores + row0 * lpad_of(d), false, st));
-      }
+      DSA_TRY(run_scores(ds, qidx, w, kidx, scores, false, st, nullptr, skip, d.n_q));
     }
     DSA_TRY(run_topk(d, scores, m, idx, st));
   }

@@ -16,6 +16,10 @@ struct IndexerParams {
   int key_chunk;      // keys per workgroup (multiple of 64)
   int write_upper;    // 1: write -inf for s > p; 0: leave those entries untouched
   const int32_t* seq_len;  // [B] per-sequence cache lengths (decode kernel only), or nullptr
+  // Rows of qidx, w and scores in memory: sequence b's scored query t is
+  // row b * T_ld + row0 + t (T_ld = 0 means T). A call that leaves the first
+  // row0 rows of every sequence unscored passes T = rows - row0, T_ld = rows.
+  int row0, T_ld;
   const float* kscale;     // fp8 keys: [B][kv_cap] per-key scales; nullptr otherwise
   // Streaming selection (prefill kernel only; zero / nullptr: plain scores).
   int kt_stride;              // > 1: score only key tiles kt_stride * j (a sample), stored

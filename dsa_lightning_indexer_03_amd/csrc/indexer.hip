@@ -50,8 +50,9 @@ struct QueryFrags {
 template <typename T, int DI, int NQ>
 __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const IndexerParams& a, int b,
                                              int t_first, int c, int g) {
-  const T* qb = static_cast<const T*>(a.qidx) + (size_t)b * a.T * a.HI * DI;
-  const float* wb = a.w + (size_t)b * a.T * a.HI;
+  const size_t row_b = (size_t)b * (a.T_ld > 0 ? a.T_ld : a.T) + a.row0;  // memory row of scored query 0
+  const T* qb = static_cast<const T*>(a.qidx) + row_b * a.HI * DI;
+  const float* wb = a.w + row_b * a.HI;
   float wr[NQ][2][4];
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
@@ -377,7 +378,9 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     load_queries<T, DI, QPW>(f, a, b, t_wave, c, g);
     const int t_mine = t_wave + jl;
     p_mine = a.q_pos0 + t_mine;
-    srow = t_mine < a.T && !STREAM ? a.scores + ((size_t)b * a.T + t_mine) * a.Lpad : nullptr;
+    srow = t_mine < a.T && !STREAM
+               ? a.scores + ((size_t)b * (a.T_ld > 0 ? a.T_ld : a.T) + a.row0 + t_mine) * a.Lpad
+               : nullptr;
     if constexpr (STREAM) {
       row_mine = t_mine < a.T ? b * a.T + t_mine : -1;
       guess_mine = row_mine >= 0 ? a.guess[row_mine] : 0u;
@@ -503,9 +506,9 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
 // index_scores are written in full; the prefill kernel writes key tiles
 // 0..ntk(qt)-1 only). One workgroup per query row.
 __global__ __launch_bounds__(256) void scores_upper_fill_kernel(IndexerParams a, UnitMap um) {
-  const int row = blockIdx.x, t = row % a.T;
+  const int row = blockIdx.x, t = row % a.T, b = row / a.T;
   const int s_from = um.ntk(t / kIdxQT) << um.lk;
-  float* srow = a.scores + (size_t)row * a.Lpad;
+  float* srow = a.scores + ((size_t)b * (a.T_ld > 0 ? a.T_ld : a.T) + a.row0 + t) * a.Lpad;
   const float ninf = fneg_inf();
   for (int s4 = s_from + 4 * threadIdx.x; s4 < a.Lpad; s4 += 4 * 256)
     *reinterpret_cast<f32x4*>(srow + s4) = f32x4{ninf, ninf, ninf, ninf};
@@ -525,7 +528,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerParams a) {
   const int p_last = q_pos0 + t_first + nq - 1;
   const int s_chunk_end = min(s_begin + a.key_chunk, a.Lpad);
   const int s_stop = min(s_chunk_end, p_last + 1);
-  float* scores_b = a.scores + (size_t)b * a.T * a.Lpad;
+  float* scores_b = a.scores + ((size_t)b * (a.T_ld > 0 ? a.T_ld : a.T) + a.row0) * a.Lpad;
   const float ninf = fneg_inf();
   const int jl = ((g & 1) << 1) | (g >> 1);
   const int t_mine = jl < nq ? t_first + jl : a.T;  // a.T: this lane stores nothing

@@ -145,8 +145,7 @@ dsa_status dsa_sparse_attention(const dsa_dims* dims, const void* q, const void*
  * written; the mask then lives in the workspace). Attention paths that
  * gather kept rows read top-k's index list directly. Queries at positions
  * below top_k keep every earlier token and are not scored (the workspace
- * holds no scores for them; no output depends on them), except in batches
- * of more than 8 sequences that also have rows to score. Needs
+ * holds no scores for them; no output depends on them). Needs
  * dsa_workspace_size(dims, DSA_OP_FORWARD) bytes of workspace. */
 dsa_status dsa_forward(const dsa_dims* dims, const void* qidx, const float* w,
                        const void* kidx, const void* q, const void* k_cache,

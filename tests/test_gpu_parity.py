@@ -244,17 +244,19 @@ EDGE = [
     # one K/V row per token at decode shape: the gather path with a single KV head
     ("mqa_decode", "bf16", 3, 2, 2998, 3000, 3000, 32, 128, 500, 32, 1, 128, False),
     # rows with p + 1 <= top_k keep every token and are not scored by the
-    # forward call: a cut leaving few rows (decode-shaped scoring at an
+    # forward call (one indexer launch over the other rows of every
+    # sequence): a cut leaving few rows (decode-shaped scoring at an
     # offset), a cut past an offset, a cut one row before the end with
-    # integer ties, the one-row-per-token path, a batch scored sequence by
-    # sequence, a batch of nine (every row scored) and a batch of
-    # sequences that keep their whole context (nothing scored)
+    # integer ties, the one-row-per-token path, batches of two and nine, a
+    # decode-shaped batch (four rows per sequence, two of them cut) and a
+    # batch of sequences that keep their whole context (nothing scored)
     ("cut_leaves_five_rows", "bf16", 1, 100, 0, 100, 100, 32, 128, 95, 8, 8, 128, False),
     ("cut_after_offset_fp32", "fp32", 1, 150, 30, 200, 210, 16, 64, 120, 4, 2, 64, False),
     ("cut_last_row_integer_ties", "bf16", 1, 130, 0, 130, 130, 32, 128, 129, 8, 8, 128, True),
     ("cut_mqa", "bf16", 1, 200, 0, 200, 200, 32, 128, 150, 32, 1, 128, False),
     ("cut_per_sequence_in_a_batch", "bf16", 2, 100, 0, 100, 100, 32, 128, 60, 8, 8, 128, False),
-    ("cut_not_taken_batch_of_nine", "fp32", 9, 40, 3, 50, 56, 8, 32, 20, 4, 2, 64, False),
+    ("cut_batch_of_nine", "fp32", 9, 40, 3, 50, 56, 8, 32, 20, 4, 2, 64, False),
+    ("cut_decode_batch", "bf16", 5, 4, 58, 62, 70, 32, 128, 60, 16, 16, 128, False),
     ("cut_everything_in_a_batch", "bf16", 3, 50, 5, 60, 64, 32, 128, 64, 8, 4, 128, False),
 ]
 
