@@ -79,6 +79,7 @@ struct TopkParams {
   int B, T, q_pos0, n_kv, Lpad, top_k;
   const int32_t* seq_len;  // [B] per-sequence cache lengths, or nullptr
   const uint32_t* row_flag;  // [B*T]: select only rows whose flag is nonzero; nullptr: all rows
+  int pair_keep;  // set by launch_topk: rows [0, pair_keep) keep every candidate and ride along with others
 };
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 

@@ -10,11 +10,21 @@
 namespace dsa {
 namespace {
 
+// Rows of up to 4096 candidates (EPT_R <= 16) keep eight workgroups per CU
+// (at most 64 registers per lane).
 template <int NW, int EPT_R, int EPT_L>
-__global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
-  // last rows first: they have the most candidates (keep-all rows, which
-  // only write, fill in behind them)
-  const int t = a.T - 1 - (int)blockIdx.x;
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(EPT_R <= 16 ? 8 : 1)))
+void topk_mask_kernel(TopkParams a) {
+  // Last rows first: they have the most candidates. When the call's first
+  // pair_keep rows keep every candidate (only writes), workgroup x also
+  // writes keep-all row x, before its own row, so those writes overlap the
+  // selections instead of running after them.
+  const int x = (int)blockIdx.x, t = a.T - 1 - x;
+  if (x < a.pair_keep) {
+    const size_t row = (size_t)blockIdx.y * a.T + x;
+    keep_all_row<NW * 64>(a, a.q_pos0 + x + 1, a.mask + row * (a.Lpad / 32),
+                          a.indices ? a.indices + row * a.top_k : nullptr);
+  }
   if (a.row_flag && a.row_flag[(size_t)blockIdx.y * a.T + t] == 0u) return;
   __shared__ TopkShared<NW, EPT_L> sh;
   topk_select_row<NW, EPT_R, EPT_L>(a, t, blockIdx.y, sh);
@@ -27,14 +37,13 @@ __global__ __launch_bounds__(NW * 64) void topk_mask_kernel(TopkParams a) {
 // on chip.
 //
 //  1. A threshold is guessed from a sample of the row (64-token segments
-//     0, 8, 16, ...): the 22-bit key prefix of the sample's
-//     (1.25 k ns / n + 16)-th largest score, so that about 1.25 k + 128 of
-//     the row's scores reach it.
-//  2. One pass over the row compacts every token whose key prefix reaches
-//     the guess into LDS, in index order (at most kLongCap tokens).
+//     0, 8, 16, ...): the sample's (1.25 k ns / n + 16)-th largest score, so
+//     that about 1.25 k + 128 of the row's scores reach it.
+//  2. One pass over the row compacts every token whose score reaches the
+//     guess into LDS, in index order (at most kLongCap tokens).
 //  3. When between k and kLongCap tokens survived, the k-th largest score of
 //     the row is the k-th largest survivor (every other score is below the
-//     guess), so a radix select over the survivors, ties to the lower index,
+//     guess), so selecting among the survivors, ties to the lower index,
 //     gives the row's selection exactly. The mask is assembled in LDS.
 //  4. Otherwise (an unrepresentative sample, or heavy ties) the workgroup
 //     finds the exact threshold by radix passes that re-read the row, and a
@@ -46,12 +55,10 @@ constexpr int kLongBlock = kLongNT * kLongEPT;  // 4096 tokens per block
 constexpr int kLongSampleEPT = kTopkMaxRow / 8 / kLongNT;  // sample elements per thread (32)
 
 struct TopkLongShared {
-  uint32_t key[kLongCap];
+  float val[kLongCap];     // survivor scores
   uint16_t idx[kLongCap];  // token indices (rows hold at most 65536 tokens)
-  uint32_t hist[2048];   // radix histograms, then the mask bitmap (<= 2048 words)
+  SelectShared<kLongNW, 1> sel;  // its histogram is also the mask bitmap (<= 2048 words)
   uint32_t wcnt[2][64];  // per (element, wave) counts of one block, double-buffered
-  uint32_t red[kLongNW];
-  uint32_t found[3];
 };
 
 // Exclusive position of this lane's flagged element e in (e, wave, lane)
@@ -84,9 +91,10 @@ __device__ __forceinline__ uint32_t ordered_positions(const uint64_t (&bal)[kLon
 // (key 0 = no token, never counted). Returns the threshold as (thr, shift):
 // the tokens kept are key >> shift > thr, plus, among key >> shift == thr,
 // all of them when all_eq, else the first `rem` in index order.
-template <typename ForEach, typename Sh>
-__device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t rank, Sh& sh,
-                                                  uint32_t& thr, int& shift_out, uint32_t& rem, bool& all_eq) {
+template <typename ForEach>
+__device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t rank, uint32_t* hist, uint32_t* red,
+                                                  uint32_t* found, uint32_t& thr, int& shift_out, uint32_t& rem,
+                                                  bool& all_eq) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, count_eq = 0;
   rem = rank;
@@ -95,35 +103,35 @@ __device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t ran
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nbins = pass == 2 ? 1024 : 2048;
     const int pshift = pass == 0 ? 32 : (pass == 1 ? 21 : 10);
-    for (int i = tid; i < nbins; i += kLongNT) sh.hist[i] = 0;
+    for (int i = tid; i < nbins; i += kLongNT) hist[i] = 0;
     __syncthreads();
     for_each([&](uint32_t k) {
       const bool cand = k != 0u && (pass == 0 || (k >> pshift) == prefix);
-      if (cand) atomicAdd(&sh.hist[(k >> shift) & (nbins - 1)], 1u);
+      if (cand) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1u);
     });
     __syncthreads();
     const int bpt = nbins / kLongNT;
     const int top = nbins - tid * bpt;
     uint32_t local = 0;
-    for (int d = top - 1; d >= top - bpt; --d) local += sh.hist[d];
-    const uint32_t incl = block_inclusive_sum<kLongNW>(local, sh.red);
+    for (int d = top - 1; d >= top - bpt; --d) local += hist[d];
+    const uint32_t incl = block_inclusive_sum<kLongNW>(local, red);
     uint32_t cum = incl - local;
     if (cum < rem && rem <= incl) {
       for (int d = top - 1; d >= top - bpt; --d) {
-        const uint32_t h = sh.hist[d];
+        const uint32_t h = hist[d];
         if (cum < rem && rem <= cum + h) {
-          sh.found[0] = (uint32_t)d;
-          sh.found[1] = cum;
-          sh.found[2] = h;
+          found[0] = (uint32_t)d;
+          found[1] = cum;
+          found[2] = h;
           break;
         }
         cum += h;
       }
     }
     __syncthreads();
-    const uint32_t d = sh.found[0];
-    rem -= sh.found[1];
-    count_eq = sh.found[2];
+    const uint32_t d = found[0];
+    rem -= found[1];
+    count_eq = found[2];
     prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
     __syncthreads();
     thr_shift = shift;
@@ -169,11 +177,11 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
   };
 
   // 1. Threshold guess from the sample (or none: every token survives).
-  uint32_t guess = 0;  // survivors: key >> 10 >= guess (and a token)
+  float guess = __uint_as_float(0xff800000u);  // survivors: score >= guess
   if (n > kLongCap) {
     const int nseg = (n + 63) / 64;
     const int ns = ((nseg + 7) / 8) * 64;  // sample slots (the last segment may be partial)
-    uint32_t skey[kLongSampleEPT];
+    float sval[kLongSampleEPT];
     {
       float v[kLongSampleEPT];
 #pragma unroll
@@ -185,20 +193,15 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
       for (int e = 0; e < kLongSampleEPT; ++e) {
         const int u = e * kLongNT + tid, s = 512 * (u >> 6) + (u & 63);
-        skey[e] = u < ns && s < n ? orderable_key(v[e]) : 0u;
+        sval[e] = u < ns && s < n ? v[e] : no_token();
       }
     }
     const uint32_t nsv = (uint32_t)(64 * (n / 512) + min(n % 512, 64));  // tokens in the sample
     const uint32_t ks = min(nsv, (uint32_t)((1.25f * (float)k * (float)nsv) / (float)n) + 16u);
-    uint32_t thr, rem;
-    int shift;
-    bool all_eq;
-    long_radix_select([&](auto f) {
+    guess = select_kth<kLongNW, 1>([&](auto f) {
 #pragma unroll
-      for (int e = 0; e < kLongSampleEPT; ++e) f(skey[e]);
-    }, ks, sh, thr, shift, rem, all_eq);
-    // the survivor test is on 22-bit prefixes: widen a shorter one
-    guess = shift >= 10 ? thr << (shift - 10) : thr >> (10 - shift);
+      for (int e = 0; e < kLongSampleEPT; ++e) f(sval[e], (uint32_t)(e * kLongNT + tid));
+    }, ks, sh.sel).val;
   }
 
   // 2. Survivors, in index order, into LDS.
@@ -210,18 +213,16 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
     for (int blk = 0; blk < nblocks; ++blk) {
       if (blk + 2 < nblocks) load_block(blk + 2, nxt2);
       uint64_t bal[kLongEPT];
-      uint32_t keys[kLongEPT], pos[kLongEPT];
+      uint32_t pos[kLongEPT];
 #pragma unroll
-      for (int e = 0; e < kLongEPT; ++e) {
-        keys[e] = block_key(blk, e, cur[e]);
-        bal[e] = ballot64(keys[e] != 0u && (keys[e] >> 10) >= guess);
-      }
+      for (int e = 0; e < kLongEPT; ++e)
+        bal[e] = ballot64(blk * kLongBlock + e * kLongNT + tid < n && cur[e] >= guess);
       const uint32_t cnt = ordered_positions(bal, pos, sh.wcnt[blk & 1]);
 #pragma unroll
       for (int e = 0; e < kLongEPT; ++e) {
         const uint32_t at = total + pos[e];
         if (((bal[e] >> lane) & 1ull) && at < (uint32_t)kLongCap) {
-          sh.key[at] = keys[e];
+          sh.val[at] = cur[e];
           sh.idx[at] = (uint16_t)(blk * kLongBlock + e * kLongNT + tid);
         }
       }
@@ -239,45 +240,44 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
     // 3. Exact selection among the survivors (index order = LDS order).
     constexpr int CE = kLongCap / kLongNT;  // survivor slots per thread (16)
     static_assert(CE == kLongEPT, "survivor slots use the block layout");
-    uint32_t thr, rem;
-    int shift;
-    bool all_eq;
-    long_radix_select([&](auto f) {
+    const KthResult th = select_kth<kLongNW, 1>([&](auto f) {
 #pragma unroll
       for (int e = 0; e < CE; ++e) {
         const uint32_t u = (uint32_t)(e * kLongNT + tid);
-        f(u < total ? sh.key[u] : 0u);
+        f(u < total ? sh.val[u] : no_token(), u);
       }
-    }, k, sh, thr, shift, rem, all_eq);
+    }, k, sh.sel);
     // tie ranks among threshold-equal survivors, then the kept flags
     uint64_t beq[kLongEPT], bsel[kLongEPT];
-    uint32_t ckey[kLongEPT], pos[kLongEPT];
+    float cval[kLongEPT];
+    uint32_t pos[kLongEPT];
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
       const uint32_t u = (uint32_t)(e * kLongNT + tid);
-      ckey[e] = u < total ? sh.key[u] : 0u;
-      beq[e] = ballot64(ckey[e] != 0u && (ckey[e] >> shift) == thr);
+      cval[e] = u < total ? sh.val[u] : no_token();  // NaN: compares false
+      beq[e] = ballot64(cval[e] == th.val);
     }
     ordered_positions(beq, pos, sh.wcnt[0]);
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
       const bool eq = (beq[e] >> lane) & 1ull;
-      const bool gt = ckey[e] != 0u && (ckey[e] >> shift) > thr;
-      bsel[e] = ballot64(gt || (eq && (all_eq || pos[e] < rem)));
+      const bool gt = cval[e] > th.val;
+      bsel[e] = ballot64(gt || (eq && (th.all_eq || pos[e] < th.rem)));
     }
-    for (int i = tid; i < nwords; i += kLongNT) sh.hist[i] = 0;  // bitmap
+    uint32_t* bitmap = sh.sel.hist[0];
+    for (int i = tid; i < nwords; i += kLongNT) bitmap[i] = 0;
     const uint32_t nsel = ordered_positions(bsel, pos, sh.wcnt[1]);
     (void)nsel;
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
       if ((bsel[e] >> lane) & 1ull) {
         const int s = sh.idx[e * kLongNT + tid];
-        atomicOr(&sh.hist[s >> 5], 1u << (s & 31));
+        atomicOr(&bitmap[s >> 5], 1u << (s & 31));
         if (irow && pos[e] < k) irow[pos[e]] = s;
       }
     }
     __syncthreads();
-    for (int i = tid; i < nwords; i += kLongNT) mrow[i] = sh.hist[i];
+    for (int i = tid; i < nwords; i += kLongNT) mrow[i] = bitmap[i];
     return;
   }
 
@@ -292,7 +292,7 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
       for (int e = 0; e < kLongEPT; ++e) f(block_key(blk, e, v[e]));
     }
-  }, k, sh, thr, shift, rem, all_eq);
+  }, k, sh.sel.hist[0], sh.sel.red, sh.sel.found, thr, shift, rem, all_eq);
   uint32_t eq_before = 0, sel_before = 0;
   for (int blk = 0; blk < nblocks; ++blk) {
     float v[kLongEPT];
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kLongNT) void stream_guess_kernel(StreamSelParams a
   long_radix_select([&](auto f) {
 #pragma unroll
     for (int e = 0; e < kLongEPT; ++e) f(skey[e]);
-  }, ks, sh, thr, shift, rem, all_eq);
+  }, ks, sh.hist, sh.red, sh.found, thr, shift, rem, all_eq);
   if (tid == 0) a.guess[row] = shift >= 10 ? thr << (shift - 10) : thr >> (10 - shift);
 }
 
@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kLongNT) void stream_select_kernel(StreamSelParams 
   bool all_eq;
   long_radix_select([&](auto f) {
     for (uint32_t j = tid; j < cnt; j += kLongNT) f(lst[j].x);
-  }, k, sh, thr, shift, rem, all_eq);
+  }, k, sh.hist, sh.red, sh.found, thr, shift, rem, all_eq);
   // ties at the threshold: the rem lowest tokens, i.e. the rem largest of
   // 65536 - token among the threshold-equal survivors (tokens are distinct)
   uint32_t tthr = 0;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kLongNT) void stream_select_kernel(StreamSelParams 
         const uint2 e = lst[j];
         f((e.x >> shift) == thr ? 65536u - e.y : 0u);
       }
-    }, rem, sh, tthr, tshift, trem, tall);
+    }, rem, sh.hist, sh.red, sh.found, tthr, tshift, trem, tall);
   }
   for (int i = tid; i < nwords; i += kLongNT) sh.hist[i] = 0u;  // bitmap
   __syncthreads();
@@ -460,16 +460,24 @@ __global__ __launch_bounds__(256) void zero_u32_kernel(uint32_t* p, size_t n) {
 
 }  // namespace
 
-hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
+hipError_t launch_topk(const TopkParams& p0, hipStream_t st) {
+  TopkParams p = p0;
   const int nmax = p.q_pos0 + p.T;  // longest candidate row in the call
+  // Rows t < top_k - q_pos0 keep every candidate. When they are at most half
+  // of the call (and every sequence shares q_pos0, and every row is wanted),
+  // each rides along with a selecting row: grid T - pair_keep.
+  const int n_keep = std::min(std::max(p.top_k - p.q_pos0, 0), p.T);
+  p.pair_keep = (!p.seq_len && !p.row_flag && n_keep > 0 && 2 * n_keep <= p.T) ? n_keep : 0;
   dim3 grid(p.T, p.B);
   // Many long rows: stream each row through a small workgroup (several rows
   // per CU) with a sampled threshold; its survivors fit the LDS for top_k up
   // to 2048.
   if (nmax > 16384 && nmax <= kTopkMaxRow && p.top_k <= 2048 && (long long)p.B * p.T >= 512) {
+    p.pair_keep = 0;
     hipLaunchKernelGGL(topk_long_kernel, grid, dim3(kLongNT), 0, st, p);
     return hipGetLastError();
   }
+  grid.x = p.T - p.pair_keep;
   // Rows are latency-bound chains of barriers and LDS histograms, so the
   // smallest workgroup that holds a row (keys in registers) wins: more rows
   // are then in flight per CU.

@@ -1,23 +1,30 @@
 // Per-row top-k selection written as a bitmask over the whole cache (and an
-// ascending index list): the workgroup-level routine shared by the top-k
-// kernel and the fused decode kernel.
+// ascending index list): the workgroup-level routines shared by the top-k
+// kernels.
 //
 // Each query keeps its top_k best-scored earlier tokens [aiaulis paras 2-3;
 // devotd section 1 table, 2048 tokens] and the selection is applied as a
 // mask over the whole cache rather than by gathering rows [aiaulis para 4;
 // devotd section 2]. Ties go to the lower token index; -0.0 equals +0.0.
 //
-// One workgroup per query row. The row's candidate scores (s <= p) are held
-// on chip as order-preserving 32-bit keys (the first EPT_R per lane in
-// registers, the rest, for the longest rows, in LDS): wave w owns tokens
-// [w*EPT*64, (w+1)*EPT*64), element e of lane l is token w*EPT*64 + e*64 + l,
-// so a wave ballot over element e is exactly one 64-bit mask word. A radix
-// select (11 + 11 + 10 bits, LDS histograms) finds the key of the k-th
-// largest score (or only its leading digits, once the bin holding it is
-// kept whole) and how many of the tokens equal to it are kept; when only
-// some of the equal tokens are kept, their ranks in index order come from
-// ballots, a per-wave prefix and a workgroup scan. The row is read from HBM
-// once.
+// Scores are held and compared as floats (NaN marks "no token"; float
+// comparison already treats -0.0 and +0.0 as equal). The k-th largest score
+// of a row (select_kth) is found in two steps:
+//  1. a histogram of 2048 bins laid linearly over the row's [min, max] score
+//     (a monotone map of the value, so bins are ordered like the scores)
+//     gives the bin holding the k-th largest score and its rank inside it;
+//     on continuous scores that bin holds a few tokens, and the bins spread
+//     the LDS atomics instead of piling them onto the handful of bins that a
+//     float's top bits would give;
+//  2. a bin of at most 64 tokens is resolved directly: its tokens are
+//     gathered into one wave's lanes and each lane counts the tokens ranked
+//     above its own (larger score, or equal score and lower index). A larger
+//     bin (heavy ties, outliers, infinities) is resolved by exact radix
+//     passes over the order-preserving 32-bit keys of its tokens (11, 11 and
+//     10 bits), down to the full key.
+// The result is the threshold score, how many of the tokens equal to it are
+// kept and whether that is all of them; kept tokens are those above it plus,
+// among those equal to it, the first ones in index order.
 #pragma once
 
 #include "dsa_device.hpp"
@@ -25,11 +32,26 @@
 
 namespace dsa {
 
-template <int NW, int EPT_L> struct TopkShared {
-  uint32_t hist[2048];
-  uint32_t lkeys[EPT_L > 0 ? EPT_L * NW * 64 : 1];  // element e >= EPT_R of thread tid
-  uint32_t red[NW];
-  uint32_t found[3];
+constexpr int kSelBins = 2048;   // histogram bins of one select pass
+constexpr int kSelDirect = 64;   // largest threshold bin resolved by ranking its tokens
+
+template <int NW, int NBUF> struct SelectShared {
+  // NBUF = 2: a pass zeroes the next pass's histogram, saving a barrier.
+  // The 64 words past the bins take the counts of lanes without a
+  // candidate (one word per lane, never read), which keeps the counting
+  // branch-free.
+  uint32_t hist[NBUF][kSelBins + 64];
+  uint32_t red[NW];               // scan partials
+  float vmm[2][NW];               // per-wave min / max score
+  uint32_t found[3];              // threshold bin, tokens in bins above it, tokens in it
+  uint32_t ncand;
+  uint2 cand[kSelDirect];         // (key, token) of the threshold bin's tokens
+};
+
+struct KthResult {
+  float val;      // the k-th largest score
+  uint32_t rem;   // tokens equal to val that are kept (the first rem in index order)
+  bool all_eq;    // every token equal to val is kept
 };
 
 // Inclusive scan over the workgroup; red must hold NW words.
@@ -47,15 +69,229 @@ __device__ __forceinline__ uint32_t block_inclusive_sum(uint32_t v, uint32_t* re
   return base + inc;
 }
 
-// Selects row t of sequence b (one workgroup of NW waves per row).
+// Whole-wave reductions and scans on DPP lane moves (the device library's
+// wave functions), cheaper than LDS-routed shuffles; every lane must be
+// active. The reductions return a wave-uniform value; the float ones skip
+// NaN.
+extern "C" __device__ float __ockl_wfred_min_f32(float);
+extern "C" __device__ float __ockl_wfred_max_f32(float);
+extern "C" __device__ uint32_t __ockl_wfscan_add_u32(uint32_t, bool);
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) { return __ockl_wfscan_add_u32(v, true); }
+
+// A value every lane holds alike, read from LDS: moved to a scalar register
+// so that loops and branches on it are uniform.
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Lanes below this one whose bit is set in a wave ballot.
+__device__ __forceinline__ uint32_t ballot_rank(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+
+// The float value of a nonzero orderable key (inverse of orderable_key).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ float no_token() { return __uint_as_float(0x7fc00000u); }
+
+// k-th largest score (k = rank >= 1) over the scores for_each visits:
+// for_each(f) calls f(score, token) for each of this thread's elements
+// (NaN = no token), with tokens distinct and ordered like the token
+// indices. At least `rank` tokens must exist. Every thread of the workgroup
+// calls it; a barrier must separate it from earlier uses of sh, and waves
+// may still read sh when it returns.
+template <int NW, int NBUF, typename ForEach>
+__device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank, SelectShared<NW, NBUF>& sh) {
+  constexpr int NT = NW * 64;
+  constexpr int BPT = kSelBins / NT;  // histogram bins scanned per thread
+  static_assert(BPT == 2 || BPT == 4 || BPT == 8, "bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t spare = (uint32_t)(kSelBins + lane);  // the count word of a lane without a candidate
+
+  // Score range of the row (compare-and-select, which skips NaN and, unlike
+  // fminf, adds no canonicalising copy of every element).
+  float lo = __uint_as_float(0x7f800000u), hi = -lo;
+  for_each([&](float v, uint32_t) {
+    lo = v < lo ? v : lo;
+    hi = v > hi ? v : hi;
+  });
+  lo = __ockl_wfred_min_f32(lo);
+  hi = __ockl_wfred_max_f32(hi);
+  for (int i = tid; i < NBUF * (kSelBins + 64); i += NT) (&sh.hist[0][0])[i] = 0u;
+  if (tid == 0) sh.ncand = 0u;
+  if (lane == 0) {
+    sh.vmm[0][wave] = lo;
+    sh.vmm[1][wave] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    lo = fminf(lo, sh.vmm[0][w]);
+    hi = fmaxf(hi, sh.vmm[1][w]);
+  }
+  lo = uniform_f32(lo);
+  hi = uniform_f32(hi);
+  // Bin of a score: linear over [min, max]. Rounded subtraction and
+  // multiplication by a positive factor never reverse an order, so the bins
+  // are ordered like the scores. A range that is empty or overflows gives a
+  // factor of inf or 0 and the products NaN or 0 (clamped and converted to
+  // bin 0), or inf (bin 2047): still ordered, and the exact passes decide.
+  const float scale = (float)kSelBins / (hi - lo);
+  auto bin_of = [lo, scale](float v) -> uint32_t {
+    return (uint32_t)fminf(fmaxf((v - lo) * scale, 0.0f), (float)(kSelBins - 1));
+  };
+  // Each pass folds its own opaque zero into the scores, so the compiler
+  // recomputes bins and keys where they are needed instead of keeping values
+  // per element live in registers across the passes.
+  auto opaque_zero = []() {
+    uint32_t z = 0u;
+    asm volatile("" : "+v"(z));
+    return z;
+  };
+
+  uint32_t rem = rank, d0 = 0, prefix = 0, count_eq = 0;
+  int shift = 0;  // key shift of the prefix matched so far (passes >= 1)
+  int dpass = 0;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    // pass 0: score bins; passes 1-3: key bits 31..21, 20..10, 9..0 of the
+    // threshold bin's tokens
+    uint32_t* h = sh.hist[NBUF == 2 ? (pass & 1) : 0];
+    if (pass > 0) {
+      if (NBUF == 1) {
+        for (int i = tid; i < kSelBins; i += NT) h[i] = 0u;
+        __syncthreads();
+      } else if (pass < 3) {  // the next pass's histogram (last read before this pass's first barrier)
+        uint32_t* hn = sh.hist[(pass + 1) & 1];
+        for (int i = tid; i < kSelBins; i += NT) hn[i] = 0u;
+      }
+    }
+    const int dshift = pass == 1 ? 21 : (pass == 2 ? 10 : 0);
+    const uint32_t dmask = pass == 3 ? 1023u : 2047u;
+    const uint32_t z = opaque_zero();
+    for_each([&](float v0, uint32_t) {
+      const float v = __uint_as_float(__float_as_uint(v0) ^ z);
+      const bool tok = v == v;
+      const uint32_t b = bin_of(v);
+      if (pass == 0) {
+        atomicAdd(&h[tok ? b : spare], 1u);
+      } else {
+        const uint32_t k = orderable_key(v);
+        const bool c = tok && b == d0 && (pass == 1 || (k >> shift) == prefix);
+        atomicAdd(&h[c ? (k >> dshift) & dmask : spare], 1u);
+      }
+    });
+    __syncthreads();
+    // Thread tid owns bins [kSelBins - (tid+1)*BPT, kSelBins - tid*BPT), highest first.
+    const int b0 = kSelBins - (tid + 1) * BPT;
+    uint32_t local = 0;
+    if constexpr (BPT == 8) {
+      const uint4 x = *reinterpret_cast<const uint4*>(h + b0), y = *reinterpret_cast<const uint4*>(h + b0 + 4);
+      local = x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w;
+    } else if constexpr (BPT == 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(h + b0);
+      local = x.x + x.y + x.z + x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(h + b0);
+      local = x.x + x.y;
+    }
+    // workgroup scan (red is next written after this pass's last barrier)
+    const uint32_t inc = wave_scan_u32(local);
+    if (lane == 63) sh.red[wave] = inc;
+    __syncthreads();
+    uint32_t cum = inc - local;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+      if (w < wave) cum += sh.red[w];
+    if (cum < rem && rem <= cum + local) {  // the one thread whose bins hold the rank
+      for (int j = BPT - 1; j >= 0; --j) {
+        const uint32_t hj = h[b0 + j];
+        if (rem <= cum + hj) {
+          sh.found[0] = (uint32_t)(b0 + j);
+          sh.found[1] = cum;
+          sh.found[2] = hj;
+          break;
+        }
+        cum += hj;
+      }
+    }
+    __syncthreads();
+    const uint32_t d = uniform_u32(sh.found[0]);
+    rem -= uniform_u32(sh.found[1]);
+    count_eq = uniform_u32(sh.found[2]);
+    if (pass == 0) {
+      d0 = d;
+    } else {
+      prefix = pass == 1 ? d : ((prefix << (pass == 2 ? 11 : 10)) | d);
+      shift = dshift;
+    }
+    if (pass == 3) return KthResult{key_value(prefix), rem, rem == count_eq};
+    if (count_eq <= (uint32_t)kSelDirect) {
+      dpass = pass;
+      break;
+    }
+  }
+
+  // Rank the threshold bin's tokens directly (dpass: the last pass taken).
+  const uint32_t zc = opaque_zero();
+  for_each([&](float v0, uint32_t id) {
+    const float v = __uint_as_float(__float_as_uint(v0) ^ zc);
+    const uint32_t k = orderable_key(v);
+    if (v == v && bin_of(v) == d0 && (dpass == 0 || (k >> shift) == prefix)) {
+      const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+      sh.cand[slot] = make_uint2(k, id);
+    }
+  });
+  __syncthreads();
+  const bool mine = (uint32_t)lane < count_eq;
+  const uint2 c = mine ? sh.cand[lane] : make_uint2(0u, 0xffffffffu);
+  uint32_t above = 0;  // tokens of the bin ranked above this lane's
+  for (uint32_t i = 0; i < count_eq; ++i) {
+    const uint32_t ki = (uint32_t)__builtin_amdgcn_readlane((int)c.x, (int)i);
+    const uint32_t ii = (uint32_t)__builtin_amdgcn_readlane((int)c.y, (int)i);
+    above += (ki > c.x || (ki == c.x && ii < c.y)) ? 1u : 0u;
+  }
+  const uint64_t at = ballot64(mine && above == rem - 1u);
+  const uint32_t tkey = (uint32_t)__builtin_amdgcn_readlane((int)c.x, (int)(__ffsll((unsigned long long)at) - 1));
+  const uint32_t gt = (uint32_t)__popcll(ballot64(mine && c.x > tkey));
+  const uint32_t eq = (uint32_t)__popcll(ballot64(mine && c.x == tkey));
+  return KthResult{key_value(tkey), rem - gt, eq == rem - gt};
+}
+
+// A row whose candidates (n of them) are all kept: mask bits [0, n), and the
+// index list 0 .. n-1 padded with -1.
+template <int NT>
+__device__ __forceinline__ void keep_all_row(const TopkParams& a, int n, uint32_t* mrow, int32_t* irow) {
+  const int nwords = a.Lpad / 32;
+  for (int wi = threadIdx.x; wi < nwords; wi += NT) {
+    const int lo = wi * 32;
+    mrow[wi] = lo + 32 <= n ? 0xffffffffu : (lo < n ? (1u << (n - lo)) - 1u : 0u);
+  }
+  if (irow)
+    for (int j = threadIdx.x; j < a.top_k; j += NT) irow[j] = j < n ? j : -1;
+}
+
+template <int NW, int EPT_L> struct TopkShared {
+  SelectShared<NW, 2> sel;
+  float lvals[EPT_L > 0 ? EPT_L * NW * 64 : 1];  // element e >= EPT_R of thread tid
+  uint32_t eqc[NW];   // per-wave threshold-equal counts
+  uint32_t selc[NW];  // per-wave kept counts
+};
+
+// Selects row t of sequence b (one workgroup of NW waves per row). The row's
+// candidate scores (s <= p) are held on chip: the first EPT_R per lane in
+// registers, the rest, for the longest rows, in LDS. Wave w owns tokens
+// [w*EPT*64, (w+1)*EPT*64), element e of lane l is token w*EPT*64 + e*64 + l,
+// so a wave ballot over element e is exactly one 64-bit mask word. The row
+// is read from HBM once.
 template <int NW, int EPT_R, int EPT_L>
 __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int b, TopkShared<NW, EPT_L>& sh) {
   constexpr int NT = NW * 64, EPT = EPT_R + EPT_L;
   static_assert(EPT_L % 16 == 0, "LDS-held elements load 16 at a time");
-  uint32_t* hist = sh.hist;
-  uint32_t* lkeys = sh.lkeys;
-  uint32_t* red = sh.red;
-  uint32_t* found = sh.found;
+  float* lvals = sh.lvals;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int q_pos0, n_kv;
@@ -68,23 +304,18 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
   int32_t* irow = a.indices ? a.indices + row * a.top_k : nullptr;
 
   if (a.top_k >= n) {  // every candidate is kept
-    for (int wi = tid; wi < nwords; wi += NT) {
-      const int lo = wi * 32;
-      mrow[wi] = lo + 32 <= n ? 0xffffffffu : (lo < n ? (1u << (n - lo)) - 1u : 0u);
-    }
-    if (irow)
-      for (int j = tid; j < a.top_k; j += NT) irow[j] = j < n ? j : -1;
+    keep_all_row<NT>(a, n, mrow, irow);
     return;
   }
 
   // Loads are unconditional (positions past the row read its last candidate,
-  // then become the "no token" key 0), so they all stay in flight together
-  // instead of each waiting behind a branch.
+  // then become "no token"), so they all stay in flight together instead of
+  // each waiting behind a branch.
   // The scheduling barriers keep each batch of loads together ahead of its
   // conversions, which the scheduler would otherwise pair one by one.
   const int base = wave * EPT * 64;
-  auto to_key = [&](float v, int idx) -> uint32_t { return idx < n ? orderable_key(v) : 0u; };
-  uint32_t rkey[EPT_R];
+  auto to_val = [&](float v, int idx) -> float { return idx < n ? v : no_token(); };
+  float rval[EPT_R];
   if (EPT_L > 0) {  // LDS-held elements first, 16 loads in flight at a time
 #pragma unroll 1
     for (int e0 = EPT_R; e0 < EPT; e0 += 16) {
@@ -93,7 +324,7 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
       for (int j = 0; j < 16; ++j) v16[j] = srow[min(base + (e0 + j) * 64 + lane, n - 1)];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 16; ++j) lkeys[(e0 + j - EPT_R) * NT + tid] = to_key(v16[j], base + (e0 + j) * 64 + lane);
+      for (int j = 0; j < 16; ++j) lvals[(e0 + j - EPT_R) * NT + tid] = to_val(v16[j], base + (e0 + j) * 64 + lane);
     }
   }
   {
@@ -102,91 +333,37 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
     for (int e = 0; e < EPT_R; ++e) v[e] = srow[min(base + e * 64 + lane, n - 1)];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int e = 0; e < EPT_R; ++e) rkey[e] = to_key(v[e], base + e * 64 + lane);
+    for (int e = 0; e < EPT_R; ++e) rval[e] = to_val(v[e], base + e * 64 + lane);
   }
   // e is a compile-time constant at every use, so this picks a register or LDS.
-  auto key = [&](int e) -> uint32_t { return e < EPT_R ? rkey[e < EPT_R ? e : 0] : lkeys[(e - EPT_R) * NT + tid]; };
+  auto val = [&](int e) -> float { return e < EPT_R ? rval[e < EPT_R ? e : 0] : lvals[(e - EPT_R) * NT + tid]; };
 
-  // Radix select of the k-th largest key.
-  uint32_t prefix = 0;
-  uint32_t rem = (uint32_t)a.top_k;  // rank of the threshold within the current candidates
-  uint32_t count_eq = 0;
-  int thr_shift = 0;  // the threshold is a prefix: keys compare as key >> thr_shift
+  const KthResult th = select_kth<NW, 2>([&](auto f) {
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nbins = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nbins; i += NT) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      // key 0 marks "no token" (no finite score maps to 0, and its high
-      // digits never equal a selected prefix, which is a finite key's).
-      const uint32_t k = key(e);
-      const bool cand = pass == 0 ? k != 0u : (pass == 1 ? (k >> 21) == prefix : (k >> 10) == prefix);
-      if (cand) atomicAdd(&hist[(k >> shift) & (nbins - 1)], 1u);
-    }
-    __syncthreads();
-    // Thread tid owns bins [nbins - (tid+1)*bpt, nbins - tid*bpt), highest first.
-    const int bpt = nbins / NT;
-    const int top = nbins - tid * bpt;
-    uint32_t local = 0;
-    for (int d = top - 1; d >= top - bpt; --d) local += hist[d];
-    const uint32_t incl = block_inclusive_sum<NW>(local, red);
-    uint32_t cum = incl - local;  // tokens in bins above this thread's range
-    if (cum < rem && rem <= incl) {
-      for (int d = top - 1; d >= top - bpt; --d) {
-        const uint32_t h = hist[d];
-        if (cum < rem && rem <= cum + h) {
-          found[0] = (uint32_t)d;
-          found[1] = cum;
-          found[2] = h;
-          break;
-        }
-        cum += h;
-      }
-    }
-    __syncthreads();
-    const uint32_t d = found[0];
-    rem -= found[1];
-    count_eq = found[2];
-    prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
-    __syncthreads();
-    // Every token of the threshold's bin is kept: the prefix already
-    // separates kept from dropped tokens, and the later digits need not be
-    // resolved (the usual case after 22 bits on continuous scores).
-    if (pass < 2 && rem == count_eq) {
-      thr_shift = shift;
-      break;
-    }
-  }
-  const uint32_t thr = prefix;
-  const bool all_eq = rem == count_eq;  // every token equal to the threshold (prefix) is kept
+    for (int e = 0; e < EPT; ++e) f(val(e), (uint32_t)(base + e * 64 + lane));
+  }, (uint32_t)a.top_k, sh.sel);
 
   // Index-order rank base of this wave's threshold-equal tokens.
   uint32_t eq_base = 0;
-  if (!all_eq) {
+  if (!th.all_eq) {
     uint32_t cnt = 0;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) cnt += __popcll(ballot64((key(e) >> thr_shift) == thr));
-    if (lane == 0) red[wave] = cnt;
+    for (int e = 0; e < EPT; ++e) cnt += __popcll(ballot64(val(e) == th.val));
+    if (lane == 0) sh.eqc[wave] = cnt;
     __syncthreads();
-    for (int w = 0; w < wave; ++w) eq_base += red[w];
-    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) eq_base += w < wave ? sh.eqc[w] : 0u;
   }
 
   // Selection of element e, in index order within the wave. The running
-  // count of threshold-equal tokens gives each tie its rank.
-  const uint64_t lt = lanemask_lt();
+  // count of threshold-equal tokens gives each tie its rank. ("No token"
+  // is NaN, which compares false.)
   auto select = [&](int e, uint32_t& running_eq) -> bool {
-    const uint32_t k = key(e);
-    // thr is a finite key's prefix: never that of the 0 sentinel, whose every
-    // prefix is 0 (finite keys are at least 0x00800000)
-    const bool eq = (k >> thr_shift) == thr;
-    bool s = (k >> thr_shift) > thr;
-    if (all_eq) return s || eq;
+    const float v = val(e);
+    if (th.all_eq) return v >= th.val;
+    const bool eq = v == th.val;
     const uint64_t be = ballot64(eq);
-    s = s || (eq && running_eq + (uint32_t)__popcll(be & lt) < rem);
+    const bool s = v > th.val || (eq && running_eq + ballot_rank(be) < th.rem);
     running_eq += (uint32_t)__popcll(be);
     return s;
   };
@@ -210,15 +387,16 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
     *reinterpret_cast<uint2*>(mrow + 2 * wp) = make_uint2(0u, 0u);
 
   if (irow) {  // exactly top_k tokens are kept here
-    if (lane == 0) red[wave] = nsel;
+    if (lane == 0) sh.selc[wave] = nsel;
     __syncthreads();
     uint32_t off = 0;
-    for (int w = 0; w < wave; ++w) off += red[w];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) off += w < wave ? sh.selc[w] : 0u;
     if (4 * a.top_k < n) {
       // Sparse rows: word pair e = lane covers tokens base + 64 lane + (0..63);
       // each lane writes the few kept tokens of its own word.
       const uint32_t cnt = (uint32_t)__popcll(my_pair);
-      uint32_t pos = off + wave_inclusive_sum(cnt) - cnt;
+      uint32_t pos = off + wave_scan_u32(cnt) - cnt;
       uint64_t bits = my_pair;
       while (bits) {
         const int bit = __ffsll((unsigned long long)bits) - 1;
@@ -234,7 +412,7 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
       for (int e = 0; e < EPT; ++e) {
         const bool sel = select(e, running_eq);
         const uint64_t bs = ballot64(sel);
-        const uint32_t pos = off + (uint32_t)__popcll(bs & lt);
+        const uint32_t pos = off + ballot_rank(bs);
         if (sel && pos < (uint32_t)a.top_k) irow[pos] = base + e * 64 + lane;
         off += (uint32_t)__popcll(bs);
       }

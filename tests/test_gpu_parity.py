@@ -364,6 +364,63 @@ def test_topk_kernel_on_crafted_scores(n_kv, T, top_k):
         assert np.array_equal(mask[i], pack_mask(sel, n_kv)), f"row {i} mask"
 
 
+def _skewed_scores(recipe, shape, rng):
+    """Score rows whose value range defeats a histogram laid linearly over
+    [min, max]: the threshold's bin then holds many tokens, and the selection
+    goes through the exact passes over key bits."""
+    s = rng.standard_normal(shape).astype(np.float32)
+    if recipe == "outliers":  # a few huge magnitudes of both signs
+        s[rng.random(shape) < 0.002] = 3e30
+        s[rng.random(shape) < 0.002] = -3e30
+    elif recipe == "infinities":
+        s[rng.random(shape) < 0.003] = np.inf
+        s[rng.random(shape) < 0.003] = -np.inf
+    elif recipe == "tiny":  # subnormal to tiny magnitudes, both signs, and zeros
+        s = (s * np.float32(1e-38)).astype(np.float32)
+        s[rng.random(shape) < 0.1] = 0.0
+        s[rng.random(shape) < 0.05] = -0.0
+    elif recipe == "two_clusters":  # two groups 1e6 apart
+        s[rng.random(shape) < 0.5] += np.float32(1e6)
+    elif recipe == "near_equal":  # values a few ulps apart: long runs of equal keys
+        s = (np.float32(1.0) + rng.integers(0, 40, size=shape).astype(np.float32) * np.float32(2.0 ** -23))
+        s = s.astype(np.float32)
+    return s
+
+
+SKEWED_TOPK = [
+    # (recipe, n_kv, T, top_k): every row-size class of the top-k kernel, and
+    # the streamed long-row kernel (>= 512 rows of more than 16384 candidates)
+    ("outliers", 2000, 40, 700), ("infinities", 4000, 40, 2048), ("tiny", 8000, 24, 2048),
+    ("two_clusters", 16000, 12, 3000), ("near_equal", 30000, 6, 2048), ("outliers", 65536, 3, 2048),
+    ("infinities", 65536, 2, 60000), ("near_equal", 3000, 64, 1500),
+    ("outliers", 20000, 512, 2048), ("two_clusters", 40000, 520, 2048), ("tiny", 30000, 512, 1024),
+]
+
+
+@pytest.mark.parametrize("recipe,n_kv,T,top_k", SKEWED_TOPK, ids=[f"{c[0]}_{c[1]}_{c[2]}" for c in SKEWED_TOPK])
+def test_topk_kernel_on_skewed_scores(recipe, n_kv, T, top_k):
+    """The top-k op alone on float32 rows with outliers, infinities,
+    subnormals, far-apart clusters or runs of equal keys: masks and index
+    lists bit-exact against the oracle's selection (every row, or 48 seeded
+    rows plus the first and last of the long-row calls)."""
+    rng = np.random.default_rng(n_kv * 7 + T)
+    q_pos0 = n_kv - T
+    L = dsa.lpad(n_kv)
+    s = _skewed_scores(recipe, (1, T, L), rng)
+    scores = torch.from_numpy(s).to(DEV)
+    mask, idx = dsa.topk_mask(scores, q_pos0=q_pos0, n_kv=n_kv, top_k=top_k)
+    torch.cuda.synchronize()
+    mask, idx = to_np(mask[0]).view(np.uint32), to_np(idx[0])
+    rows = range(T) if T <= 64 else sorted({0, T - 1} | set(rng.choice(T, 48, replace=False).tolist()))
+    for i in rows:
+        p = q_pos0 + i
+        sel = select_topk(round_scores_fp32(s[0, i]), p, top_k)
+        want = np.full(top_k, -1, dtype=np.int32)
+        want[: len(sel)] = sel
+        assert np.array_equal(idx[i], want), f"{recipe} row {i}"
+        assert np.array_equal(mask[i], pack_mask(sel, n_kv)), f"{recipe} row {i} mask"
+
+
 LONG_TOPK = [
     # name, T, n_kv, top_k, score recipe; every call has > 16384 candidates in
     # its longest row and >= 512 rows, the shape of the streamed long-row top-k
