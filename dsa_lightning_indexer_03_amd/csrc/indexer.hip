@@ -44,9 +44,12 @@ struct QueryFrags {
 };
 
 // Loads the A fragments and head weights of queries t_first .. t_first+NQ-1.
-// Queries past T and heads past H_I read a valid row (finite data) and get
-// weight 0, so they add exact zeros. Every load is unconditional and issued
-// before any of them is used, so they all share one memory round trip.
+// Queries past T and heads past H_I read a valid row (finite data). Heads
+// past H_I get weight 0, so they add exact zeros to their query's sum; a
+// query past T only lands in lanes whose score is never stored, so its
+// weights stay as loaded. Every load is unconditional and issued before any
+// of them is used, so they all share one memory round trip; with 32 or more
+// heads nothing waits for them here.
 template <typename T, int DI, int NQ>
 __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const IndexerParams& a, int b,
                                              int t_first, int c, int g) {
@@ -54,6 +57,8 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
   const T* qb = static_cast<const T*>(a.qidx) + row_b * a.HI * DI;
   const float* wb = a.w + row_b * a.HI;
   float wr[NQ][2][4];
+  // 32 heads: the four weights of heads 16*rb + 4*g + (0..3) are one aligned 16-byte load
+  const bool all_heads = a.HI == 32 && ((reinterpret_cast<uintptr_t>(wb) & 15) == 0);
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
     const int tc = min(t_first + j, a.T - 1);
@@ -64,8 +69,14 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
       for (int kk = 0; kk < QueryFrags<T, DI, NQ>::KSTEPS; ++kk)
         f.a[j][rb][kk] = load_frag<T>(qb + ((size_t)tc * a.HI + head) * DI + frag_off<T>(kk, g));
       // weights of heads 16*rb + 4*g + (0..3)
+      if (all_heads) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(wb + (size_t)tc * 32 + 16 * rb + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) wr[j][rb][r] = wb[(size_t)tc * a.HI + min(16 * rb + 4 * g + r, a.HI - 1)];
+        for (int r = 0; r < 4; ++r) wr[j][rb][r] = w4[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wr[j][rb][r] = wb[(size_t)tc * a.HI + min(16 * rb + 4 * g + r, a.HI - 1)];
+      }
     }
   }
 #pragma unroll
@@ -74,7 +85,7 @@ __device__ __forceinline__ void load_queries(QueryFrags<T, DI, NQ>& f, const Ind
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        f.w[j][rb][r] = (t_first + j < a.T && 16 * rb + 4 * g + r < a.HI) ? wr[j][rb][r] : 0.f;
+        f.w[j][rb][r] = all_heads ? wr[j][rb][r] : (16 * rb + 4 * g + r < a.HI ? wr[j][rb][r] : 0.f);
 }
 
 // Scores of the wave's (up to 4) queries against one 16-key subtile whose B
@@ -386,9 +397,8 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       guess_mine = row_mine >= 0 ? a.guess[row_mine] : 0u;
     }
   };
-  // the first query tile's fragments travel with the prologue's key tiles
-  switch_tile(b, um.qt_at(qp));
-  // Prologue: tiles of units u0 .. u0+S-2 (clamped to the range's last unit).
+  // Prologue: tiles of units u0 .. u0+S-2 (clamped to the range's last
+  // unit), then the first query tile's fragments, all in flight together.
   int pb = b, ppos = qp, pkt = kt;  // prefetch cursor: the unit whose tile was loaded last
   long long pu = u0;
   dload(pb, pkt, 0);
@@ -400,6 +410,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
     }
     dload(pb, pkt, i);
   }
+  switch_tile(b, um.qt_at(qp));
 
   auto flush = [&]() {
     if constexpr (STREAM) {
@@ -444,7 +455,9 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       }
     }
   };
-  // tile of u0 landed: the S-2 later tiles may still be in flight
+  // tile of u0 landed (the S-2 later tiles may still be in flight; the query
+  // loads issued after them are then mostly done too, and the first scores
+  // wait for the rest)
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NLD));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
