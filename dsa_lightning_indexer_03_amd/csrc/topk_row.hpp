@@ -97,6 +97,11 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 __device__ __forceinline__ float no_token() { return __uint_as_float(0x7fc00000u); }
 
+// Word 3 of a raw buffer descriptor on gfx9-family GPUs (32-bit data format,
+// no swizzle): loads past the descriptor's byte count return 0 and stores
+// past it are dropped.
+constexpr int kBufferWord3 = 0x00020000;
+
 // k-th largest score (k = rank >= 1) over the scores for_each visits:
 // for_each(f) calls f(score, token) for each of this thread's elements
 // (NaN = no token), with tokens distinct and ordered like the token
@@ -173,7 +178,9 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
     const uint32_t dmask = pass == 3 ? 1023u : 2047u;
     const uint32_t z = opaque_zero();
     for_each([&](float v0, uint32_t) {
-      const float v = __uint_as_float(__float_as_uint(v0) ^ z);
+      // pass 0 takes the scores as they are (the later passes and the
+      // gather below fold in their own zero)
+      const float v = pass == 0 ? v0 : __uint_as_float(__float_as_uint(v0) ^ z);
       const bool tok = v == v;
       const uint32_t b = bin_of(v);
       if (pass == 0) {
@@ -236,15 +243,26 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
   }
 
   // Rank the threshold bin's tokens directly (dpass: the last pass taken).
+  // Keys are formed only for the bin's tokens.
   const uint32_t zc = opaque_zero();
-  for_each([&](float v0, uint32_t id) {
-    const float v = __uint_as_float(__float_as_uint(v0) ^ zc);
-    const uint32_t k = orderable_key(v);
-    if (v == v && bin_of(v) == d0 && (dpass == 0 || (k >> shift) == prefix)) {
-      const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-      sh.cand[slot] = make_uint2(k, id);
-    }
-  });
+  if (dpass == 0) {
+    for_each([&](float v0, uint32_t id) {
+      const float v = __uint_as_float(__float_as_uint(v0) ^ zc);
+      if (v == v && bin_of(v) == d0) {
+        const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+        sh.cand[slot] = make_uint2(orderable_key(v), id);
+      }
+    });
+  } else {
+    for_each([&](float v0, uint32_t id) {
+      const float v = __uint_as_float(__float_as_uint(v0) ^ zc);
+      const uint32_t k = orderable_key(v);
+      if (v == v && bin_of(v) == d0 && (k >> shift) == prefix) {
+        const uint32_t slot = atomicAdd(&sh.ncand, 1u);
+        sh.cand[slot] = make_uint2(k, id);
+      }
+    });
+  }
   __syncthreads();
   const bool mine = (uint32_t)lane < count_eq;
   const uint2 c = mine ? sh.cand[lane] : make_uint2(0u, 0xffffffffu);
@@ -313,7 +331,16 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
   // each waiting behind a branch.
   // The scheduling barriers keep each batch of loads together ahead of its
   // conversions, which the scheduler would otherwise pair one by one.
+  // The row is read through a buffer descriptor bounded to its n
+  // candidates: one offset register per lane, each element's 256-byte step
+  // in the instruction's immediate offset, and loads past the row return 0
+  // (then marked "no token"), so every load is unconditional and they all
+  // stay in flight together. The scheduling barriers keep each batch of
+  // loads together ahead of its conversions, which the scheduler would
+  // otherwise pair one by one.
   const int base = wave * EPT * 64;
+  const __amdgpu_buffer_rsrc_t srsrc = __builtin_amdgcn_make_buffer_rsrc((void*)srow, (short)0, n * 4, kBufferWord3);
+  const int voff = (base + lane) * 4;
   auto to_val = [&](float v, int idx) -> float { return idx < n ? v : no_token(); };
   float rval[EPT_R];
   if (EPT_L > 0) {  // LDS-held elements first, 16 loads in flight at a time
@@ -321,7 +348,8 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
     for (int e0 = EPT_R; e0 < EPT; e0 += 16) {
       float v16[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v16[j] = srow[min(base + (e0 + j) * 64 + lane, n - 1)];
+      for (int j = 0; j < 16; ++j)
+        v16[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srsrc, voff + (e0 + j) * 256, 0, 0));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 16; ++j) lvals[(e0 + j - EPT_R) * NT + tid] = to_val(v16[j], base + (e0 + j) * 64 + lane);
@@ -330,7 +358,7 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
   {
     float v[EPT_R];
 #pragma unroll
-    for (int e = 0; e < EPT_R; ++e) v[e] = srow[min(base + e * 64 + lane, n - 1)];
+    for (int e = 0; e < EPT_R; ++e) v[e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srsrc, voff + e * 256, 0, 0));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int e = 0; e < EPT_R; ++e) rval[e] = to_val(v[e], base + e * 64 + lane);
@@ -406,14 +434,17 @@ __device__ __forceinline__ void topk_select_row(const TopkParams& a, int t, int 
       }
     } else {
       // Dense rows: element by element, consecutive lanes writing consecutive
-      // positions.
+      // positions, through a descriptor bounded to the list's top_k entries:
+      // lanes that keep nothing store past its end, which the hardware drops.
+      const __amdgpu_buffer_rsrc_t irsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)irow, (short)0, a.top_k * 4, kBufferWord3);
       running_eq = eq_base;
 #pragma unroll
       for (int e = 0; e < EPT; ++e) {
         const bool sel = select(e, running_eq);
         const uint64_t bs = ballot64(sel);
-        const uint32_t pos = off + ballot_rank(bs);
-        if (sel && pos < (uint32_t)a.top_k) irow[pos] = base + e * 64 + lane;
+        const uint32_t pos = sel ? off + ballot_rank(bs) : 0x3fffffffu;
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)(base + e * 64 + lane), irsrc, (int)(pos * 4u), 0, 0);
         off += (uint32_t)__popcll(bs);
       }
     }
