@@ -37,8 +37,9 @@ void topk_mask_kernel(TopkParams a) {
 // on chip.
 //
 //  1. A threshold is guessed from a sample of the row (64-token segments
-//     0, 8, 16, ...): the sample's (1.25 k ns / n + 16)-th largest score, so
-//     that about 1.25 k + 128 of the row's scores reach it.
+//     0, 16, 32, ...): the sample's (1.25 k ns / n + 16)-th largest score, so
+//     that about 1.25 k + 256 of the row's scores reach it. The row's first
+//     block of loads is already in flight meanwhile.
 //  2. One pass over the row compacts every token whose score reaches the
 //     guess into LDS, in index order (at most kLongCap tokens).
 //  3. When between k and kLongCap tokens survived, the k-th largest score of
@@ -52,7 +53,8 @@ constexpr int kLongNW = 4, kLongNT = kLongNW * 64;
 constexpr int kLongCap = 4096;               // survivors held in LDS
 constexpr int kLongEPT = 16;                 // row elements per thread per block
 constexpr int kLongBlock = kLongNT * kLongEPT;  // 4096 tokens per block
-constexpr int kLongSampleEPT = kTopkMaxRow / 8 / kLongNT;  // sample elements per thread (32)
+constexpr int kLongSampleSeg = 16;  // the sample takes every 16th 64-token segment
+constexpr int kLongSampleEPT = kTopkMaxRow / kLongSampleSeg / kLongNT;  // sample elements per thread (16)
 
 struct TopkLongShared {
   float val[kLongCap];     // survivor scores
@@ -176,27 +178,33 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
     return blk * kLongBlock + e * kLongNT + tid < n ? orderable_key(v) : 0u;
   };
 
+  // The row's first block is requested before anything else, so that its
+  // loads are in flight while the sample is selected.
+  float cur[kLongEPT];
+  load_block(0, cur);
+
   // 1. Threshold guess from the sample (or none: every token survives).
   float guess = __uint_as_float(0xff800000u);  // survivors: score >= guess
   if (n > kLongCap) {
+    constexpr int SPAN = 64 * kLongSampleSeg;  // tokens from one sampled segment to the next
     const int nseg = (n + 63) / 64;
-    const int ns = ((nseg + 7) / 8) * 64;  // sample slots (the last segment may be partial)
+    const int ns = ((nseg + kLongSampleSeg - 1) / kLongSampleSeg) * 64;  // sample slots (the last segment may be partial)
     float sval[kLongSampleEPT];
     {
       float v[kLongSampleEPT];
 #pragma unroll
       for (int e = 0; e < kLongSampleEPT; ++e) {
         const int u = e * kLongNT + tid;
-        v[e] = srow[min(512 * (u >> 6) + (u & 63), n - 1)];
+        v[e] = srow[min(SPAN * (u >> 6) + (u & 63), n - 1)];
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int e = 0; e < kLongSampleEPT; ++e) {
-        const int u = e * kLongNT + tid, s = 512 * (u >> 6) + (u & 63);
+        const int u = e * kLongNT + tid, s = SPAN * (u >> 6) + (u & 63);
         sval[e] = u < ns && s < n ? v[e] : no_token();
       }
     }
-    const uint32_t nsv = (uint32_t)(64 * (n / 512) + min(n % 512, 64));  // tokens in the sample
+    const uint32_t nsv = (uint32_t)(64 * (n / SPAN) + min(n % SPAN, 64));  // tokens in the sample
     const uint32_t ks = min(nsv, (uint32_t)((1.25f * (float)k * (float)nsv) / (float)n) + 16u);
     guess = select_kth<kLongNW, 1>([&](auto f) {
 #pragma unroll
@@ -207,8 +215,7 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
   // 2. Survivors, in index order, into LDS.
   uint32_t total = 0;
   {
-    float cur[kLongEPT], nxt[kLongEPT], nxt2[kLongEPT];
-    load_block(0, cur);
+    float nxt[kLongEPT], nxt2[kLongEPT];
     if (nblocks > 1) load_block(1, nxt);
     for (int blk = 0; blk < nblocks; ++blk) {
       if (blk + 2 < nblocks) load_block(blk + 2, nxt2);

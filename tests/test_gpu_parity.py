@@ -426,8 +426,8 @@ LONG_TOPK = [
     # its longest row and >= 512 rows, the shape of the streamed long-row top-k
     ("random", 600, 40000, 2048, "normal"),
     ("random_k100", 520, 65536, 100, "normal"),
-    # the sampled segments (64-token segments 0, 8, 16, ...) hold the best
-    # scores, so the sampled threshold keeps too few tokens: exact fallback
+    # every 8th 64-token segment, which includes every sampled one, holds the
+    # best scores, so the sampled threshold keeps too few tokens: exact fallback
     ("sample_misses", 520, 30000, 2048, "boost_sampled"),
     # one value everywhere (and +-0): every token survives the guess (overflow)
     ("all_equal", 512, 20000, 2048, "constant"),
