@@ -243,14 +243,16 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
   }
 
   // Rank the threshold bin's tokens directly (dpass: the last pass taken).
-  // Keys are formed only for the bin's tokens.
+  // Keys are formed only for the bin's tokens. The gather recomputes the
+  // histogram's bins with the same arithmetic, so exactly count_eq tokens
+  // arrive; the slot bound only keeps the writes inside the array.
   const uint32_t zc = opaque_zero();
   if (dpass == 0) {
     for_each([&](float v0, uint32_t id) {
       const float v = __uint_as_float(__float_as_uint(v0) ^ zc);
       if (v == v && bin_of(v) == d0) {
         const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-        sh.cand[slot] = make_uint2(orderable_key(v), id);
+        if (slot < (uint32_t)kSelDirect) sh.cand[slot] = make_uint2(orderable_key(v), id);
       }
     });
   } else {
@@ -259,7 +261,7 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
       const uint32_t k = orderable_key(v);
       if (v == v && bin_of(v) == d0 && (k >> shift) == prefix) {
         const uint32_t slot = atomicAdd(&sh.ncand, 1u);
-        sh.cand[slot] = make_uint2(k, id);
+        if (slot < (uint32_t)kSelDirect) sh.cand[slot] = make_uint2(k, id);
       }
     });
   }
