@@ -62,8 +62,8 @@ dsa_status check_dims(const dsa_dims* d, bool need_idx, bool need_attn, bool nee
     return fail(DSA_ERR_SHAPE, "need q_pos0 + n_q (%lld) <= n_kv (%d)", (long long)d->q_pos0 + d->n_q, d->n_kv);
   if (d->kv_capacity < d->n_kv) return fail(DSA_ERR_SHAPE, "kv_capacity (%d) < n_kv (%d)", d->kv_capacity, d->n_kv);
   if (d->dtype != DSA_FP32 && d->dtype != DSA_BF16) return fail(DSA_ERR_UNSUPPORTED, "dtype %d not supported", d->dtype);
-  if (d->n_kv > dsa::kTopkMaxRow)
-    return fail(DSA_ERR_UNSUPPORTED, "n_kv %d above the supported maximum %d", d->n_kv, dsa::kTopkMaxRow);
+  if (d->n_kv > dsa::kTopkMaxRowBig)
+    return fail(DSA_ERR_UNSUPPORTED, "n_kv %d above the supported maximum %d", d->n_kv, dsa::kTopkMaxRowBig);
   if ((int64_t)d->batch * d->n_q > (1ll << 30)) return fail(DSA_ERR_SHAPE, "batch * n_q too large");
   if (need_idx) {
     if (d->idx_heads < 1 || d->idx_heads > 32)

@@ -166,5 +166,7 @@ hipError_t launch_mask_compact(const CompactParams& p, hipStream_t st);
 
 // Largest row length (p + 1) the top-k kernel holds in registers.
 constexpr int kTopkMaxRow = 65536;
+// Largest row length of all: longer rows than kTopkMaxRow are streamed.
+constexpr int kTopkMaxRowBig = 262144;
 
 }  // namespace dsa

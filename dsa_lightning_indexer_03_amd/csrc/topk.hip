@@ -56,12 +56,23 @@ constexpr int kLongBlock = kLongNT * kLongEPT;  // 4096 tokens per block
 constexpr int kLongSampleSeg = 16;  // the sample takes every 16th 64-token segment
 constexpr int kLongSampleEPT = kTopkMaxRow / kLongSampleSeg / kLongNT;  // sample elements per thread (16)
 
-struct TopkLongShared {
+// Rows of up to kTopkMaxRow tokens, or (BIG) up to kTopkMaxRowBig.
+template <bool BIG> struct TopkLongShared;
+template <> struct TopkLongShared<false> {
   float val[kLongCap];     // survivor scores
   uint16_t idx[kLongCap];  // token indices (rows hold at most 65536 tokens)
   SelectShared<kLongNW, 1> sel;  // its histogram is also the mask bitmap (<= 2048 words)
   uint32_t wcnt[2][64];  // per (element, wave) counts of one block, double-buffered
 };
+// Rows past 65536 tokens: 32-bit token indices, and the mask bitmap (up to
+// 8192 words) overlays the survivors' scores and indices once they have been
+// taken into registers.
+template <> struct TopkLongShared<true> {
+  uint32_t vi[2 * kLongCap];  // survivor scores (as float), then token indices; later the mask bitmap
+  SelectShared<kLongNW, 1> sel;
+  uint32_t wcnt[2][64];
+};
+static_assert(kTopkMaxRowBig / 32 <= 2 * kLongCap, "the bitmap fits over the survivor arrays");
 
 // Exclusive position of this lane's flagged element e in (e, wave, lane)
 // order, for kLongEPT elements per thread; returns the block total. wc is a
@@ -144,10 +155,22 @@ __device__ __forceinline__ void long_radix_select(ForEach for_each, uint32_t ran
   all_eq = rem == count_eq;
 }
 
-__global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) void topk_long_kernel(TopkParams a) {
+template <bool BIG>
+__global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(BIG ? 3 : 4))) void topk_long_kernel(TopkParams a) {
   const int t = a.T - 1 - (int)blockIdx.x, b = blockIdx.y;  // longest rows first
   if (a.row_flag && a.row_flag[(size_t)b * a.T + t] == 0u) return;
-  __shared__ TopkLongShared sh;
+  __shared__ TopkLongShared<BIG> sh;
+  float* lval;  // survivor scores in LDS
+  if constexpr (BIG) lval = reinterpret_cast<float*>(sh.vi);
+  else lval = sh.val;
+  auto set_idx = [&](uint32_t at, uint32_t token) {
+    if constexpr (BIG) sh.vi[kLongCap + at] = token;
+    else sh.idx[at] = (uint16_t)token;
+  };
+  auto get_idx = [&](uint32_t at) -> int {
+    if constexpr (BIG) return (int)sh.vi[kLongCap + at];
+    else return (int)sh.idx[at];
+  };
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int q_pos0, n_kv;
   seq_extent(a.seq_len, b, a.T, a.q_pos0, a.n_kv, q_pos0, n_kv);
@@ -179,38 +202,45 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
   };
 
   // The row's first block is requested before anything else, so that its
-  // loads are in flight while the sample is selected.
+  // loads are in flight while the sample is selected (rows past 65536 tokens
+  // need those registers for their larger sample).
   float cur[kLongEPT];
-  load_block(0, cur);
+  if constexpr (!BIG) load_block(0, cur);
 
-  // 1. Threshold guess from the sample (or none: every token survives).
+  // 1. Threshold guess from the sample (or none: every token survives). The
+  // sample is every stride-th 64-token segment: stride 16 for rows of up to
+  // 65536 tokens, else the smallest stride that keeps it within 128 segments.
   float guess = __uint_as_float(0xff800000u);  // survivors: score >= guess
   if (n > kLongCap) {
-    constexpr int SPAN = 64 * kLongSampleSeg;  // tokens from one sampled segment to the next
+    constexpr int SEPT = BIG ? 2 * kLongSampleEPT : kLongSampleEPT;  // sample slots per thread
     const int nseg = (n + 63) / 64;
-    const int ns = ((nseg + kLongSampleSeg - 1) / kLongSampleSeg) * 64;  // sample slots (the last segment may be partial)
-    float sval[kLongSampleEPT];
+    int stride = kLongSampleSeg;
+    if constexpr (BIG) stride = (nseg + SEPT * kLongNT / 64 - 1) / (SEPT * kLongNT / 64);
+    const int span = 64 * stride;  // tokens from one sampled segment to the next
+    const int ns = ((nseg + stride - 1) / stride) * 64;  // sample slots (the last segment may be partial)
+    float sval[SEPT];
     {
-      float v[kLongSampleEPT];
+      float v[SEPT];
 #pragma unroll
-      for (int e = 0; e < kLongSampleEPT; ++e) {
+      for (int e = 0; e < SEPT; ++e) {
         const int u = e * kLongNT + tid;
-        v[e] = srow[min(SPAN * (u >> 6) + (u & 63), n - 1)];
+        v[e] = srow[min(span * (u >> 6) + (u & 63), n - 1)];
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int e = 0; e < kLongSampleEPT; ++e) {
-        const int u = e * kLongNT + tid, s = SPAN * (u >> 6) + (u & 63);
+      for (int e = 0; e < SEPT; ++e) {
+        const int u = e * kLongNT + tid, s = span * (u >> 6) + (u & 63);
         sval[e] = u < ns && s < n ? v[e] : no_token();
       }
     }
-    const uint32_t nsv = (uint32_t)(64 * (n / SPAN) + min(n % SPAN, 64));  // tokens in the sample
+    const uint32_t nsv = (uint32_t)(64 * (n / span) + min(n % span, 64));  // tokens in the sample
     const uint32_t ks = min(nsv, (uint32_t)((1.25f * (float)k * (float)nsv) / (float)n) + 16u);
     guess = select_kth<kLongNW, 1>([&](auto f) {
 #pragma unroll
-      for (int e = 0; e < kLongSampleEPT; ++e) f(sval[e], (uint32_t)(e * kLongNT + tid));
+      for (int e = 0; e < SEPT; ++e) f(sval[e], (uint32_t)(e * kLongNT + tid));
     }, ks, sh.sel).val;
   }
+  if constexpr (BIG) load_block(0, cur);
 
   // 2. Survivors, in index order, into LDS.
   uint32_t total = 0;
@@ -229,8 +259,8 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
       for (int e = 0; e < kLongEPT; ++e) {
         const uint32_t at = total + pos[e];
         if (((bal[e] >> lane) & 1ull) && at < (uint32_t)kLongCap) {
-          sh.val[at] = cur[e];
-          sh.idx[at] = (uint16_t)(blk * kLongBlock + e * kLongNT + tid);
+          lval[at] = cur[e];
+          set_idx(at, (uint32_t)(blk * kLongBlock + e * kLongNT + tid));
         }
       }
       total += cnt;
@@ -251,40 +281,47 @@ __global__ __launch_bounds__(kLongNT) __attribute__((amdgpu_waves_per_eu(4))) vo
 #pragma unroll
       for (int e = 0; e < CE; ++e) {
         const uint32_t u = (uint32_t)(e * kLongNT + tid);
-        f(u < total ? sh.val[u] : no_token(), u);
+        f(u < total ? lval[u] : no_token(), u);
       }
     }, k, sh.sel);
     // tie ranks among threshold-equal survivors, then the kept flags
     uint64_t beq[kLongEPT], bsel[kLongEPT];
     float cval[kLongEPT];
     uint32_t pos[kLongEPT];
+    int cid[BIG ? kLongEPT : 1];  // token ids, taken before the bitmap overwrites them
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
       const uint32_t u = (uint32_t)(e * kLongNT + tid);
-      cval[e] = u < total ? sh.val[u] : no_token();  // NaN: compares false
+      cval[e] = u < total ? lval[u] : no_token();  // NaN: compares false
+      if constexpr (BIG) cid[e] = get_idx(u & (kLongCap - 1));
       beq[e] = ballot64(cval[e] == th.val);
     }
-    ordered_positions(beq, pos, sh.wcnt[0]);
+    ordered_positions(beq, pos, sh.wcnt[0]);  // its barrier ends every read of the survivor arrays
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
       const bool eq = (beq[e] >> lane) & 1ull;
       const bool gt = cval[e] > th.val;
       bsel[e] = ballot64(gt || (eq && (th.all_eq || pos[e] < th.rem)));
     }
-    uint32_t* bitmap = sh.sel.hist[0];
-    for (int i = tid; i < nwords; i += kLongNT) bitmap[i] = 0;
+    uint32_t* bitmap;
+    if constexpr (BIG) bitmap = sh.vi;
+    else bitmap = sh.sel.hist[0];
+    const int nbw = (n + 31) / 32;  // bitmap words (the rest of the mask row is zero)
+    for (int i = tid; i < nbw; i += kLongNT) bitmap[i] = 0;
     const uint32_t nsel = ordered_positions(bsel, pos, sh.wcnt[1]);
     (void)nsel;
 #pragma unroll
     for (int e = 0; e < CE; ++e) {
       if ((bsel[e] >> lane) & 1ull) {
-        const int s = sh.idx[e * kLongNT + tid];
+        int s;
+        if constexpr (BIG) s = cid[e];
+        else s = get_idx(e * kLongNT + tid);
         atomicOr(&bitmap[s >> 5], 1u << (s & 31));
         if (irow && pos[e] < k) irow[pos[e]] = s;
       }
     }
     __syncthreads();
-    for (int i = tid; i < nwords; i += kLongNT) mrow[i] = bitmap[i];
+    for (int i = tid; i < nwords; i += kLongNT) mrow[i] = i < nbw ? bitmap[i] : 0u;
     return;
   }
 
@@ -481,7 +518,15 @@ hipError_t launch_topk(const TopkParams& p0, hipStream_t st) {
   // to 2048.
   if (nmax > 16384 && nmax <= kTopkMaxRow && p.top_k <= 2048 && (long long)p.B * p.T >= 512) {
     p.pair_keep = 0;
-    hipLaunchKernelGGL(topk_long_kernel, grid, dim3(kLongNT), 0, st, p);
+    hipLaunchKernelGGL(topk_long_kernel<false>, grid, dim3(kLongNT), 0, st, p);
+    return hipGetLastError();
+  }
+  // Rows past the register-resident limit always stream (any row count or
+  // top_k: survivors beyond the LDS take the exact passes over the row).
+  if (nmax > kTopkMaxRow) {
+    if (nmax > kTopkMaxRowBig || p.Lpad > kTopkMaxRowBig) return hipErrorInvalidValue;
+    p.pair_keep = 0;
+    hipLaunchKernelGGL(topk_long_kernel<true>, grid, dim3(kLongNT), 0, st, p);
     return hipGetLastError();
   }
   grid.x = p.T - p.pair_keep;

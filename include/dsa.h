@@ -82,7 +82,7 @@ typedef enum {
  * Supported: dtype in {DSA_FP32, DSA_BF16}; idx_dim in {32, 64, 128} for bf16
  * and {32, 64} for fp32;
  * head_dim in {64, 128}; 1 <= idx_heads <= 32; heads % kv_heads == 0;
- * n_kv <= 65536 and q_pos0 + n_q <= n_kv <= kv_capacity; top_k >= 1.
+ * n_kv <= 262144 and q_pos0 + n_q <= n_kv <= kv_capacity; top_k >= 1.
  * The configuration of the pages is idx_heads 32, idx_dim 128, top_k 2048
  * [aiu "What happened"; devotd section 1 table]. */
 typedef struct {

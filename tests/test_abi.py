@@ -68,7 +68,7 @@ def _err():
         (dict(idx_dim=96), ERR_UNSUPPORTED),
         (dict(idx_dim=128, dtype=dsa.DSA_FP32), ERR_UNSUPPORTED),
         (dict(dtype=7), ERR_UNSUPPORTED),
-        (dict(n_kv=65600, kv_capacity=65600), ERR_UNSUPPORTED),
+        (dict(n_kv=262145, kv_capacity=262145), ERR_UNSUPPORTED),
     ],
 )
 def test_index_scores_rejects_bad_dims(kw, status):

@@ -498,6 +498,112 @@ def test_topk_long_rows_streamed(case):
         assert np.array_equal(m_h[j], pack_mask(sel, n_kv)), f"{name} row {i} mask"
 
 
+BIG_TOPK = [
+    # name, T, n_kv, top_k, score recipe: rows past 65536 tokens, which the
+    # streamed kernel takes whatever the row count and top_k
+    ("random_100000", 4, 100000, 2048, "normal"),
+    ("random_262144_k100", 3, 262144, 100, "normal"),
+    # top_k past the LDS survivor capacity: exact passes over the row
+    ("random_150000_k4000", 2, 150000, 4000, "normal"),
+    # the first row keeps every candidate, the second all but one
+    ("k_near_row_70000", 2, 70000, 69999, "normal"),
+    # every 13th 64-token segment holds the best scores; 13 is the sample's
+    # stride at 100000 tokens, so the sample is all best scores and the guess
+    # keeps too few tokens: exact fallback
+    ("sample_misses_100000", 3, 100000, 2048, "boost_every_13"),
+    # huge tie groups and one value everywhere: survivors overflow the LDS
+    ("integer_ties_70000", 4, 70000, 2048, "integers"),
+    ("all_equal_200000", 2, 200000, 2048, "constant"),
+    # many rows at once (seeded sample of rows checked)
+    ("many_rows_70000", 520, 70000, 2048, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", BIG_TOPK, ids=[c[0] for c in BIG_TOPK])
+def test_topk_rows_past_65536(case):
+    """The top-k op on rows of 65537 to 262144 candidates (32-bit survivor
+    indices, a sample at a stride sized to the row, the mask bitmap laid over
+    the survivor arrays): masks and index lists bit-exact against the
+    oracle's selection on the same float32 scores."""
+    name, T, n_kv, top_k, recipe = case
+    q_pos0 = n_kv - T
+    L = dsa.lpad(n_kv)
+    if recipe.startswith("boost_every_"):
+        m = int(recipe.rsplit("_", 1)[1])
+        scores = _long_topk_scores("normal", T, L, q_pos0, zlib.crc32(name.encode()))
+        tok = torch.arange(L, device=DEV)
+        scores[:, :, (tok // 64) % m == 0] += 10.0
+    else:
+        scores = _long_topk_scores(recipe, T, L, q_pos0, zlib.crc32(name.encode()))
+    mask, idx = dsa.topk_mask(scores, q_pos0=q_pos0, n_kv=n_kv, top_k=top_k)
+    torch.cuda.synchronize()
+    rows = range(T) if T <= 8 else sorted({0, T - 1} | set(np.random.default_rng(3).choice(T, 40, replace=False).tolist()))
+    rsel = torch.as_tensor(list(rows), device=DEV)
+    s_h = to_np(scores[0, rsel])
+    m_h = to_np(mask[0, rsel]).view(np.uint32)
+    i_h = to_np(idx[0, rsel])
+    for j, i in enumerate(rows):
+        p = q_pos0 + i
+        sel = select_topk(round_scores_fp32(s_h[j]), p, top_k)
+        want = np.full(top_k, -1, dtype=np.int32)
+        want[: len(sel)] = sel
+        assert np.array_equal(i_h[j], want), f"{name} row {i}"
+        assert np.array_equal(m_h[j], pack_mask(sel, n_kv)), f"{name} row {i} mask"
+
+
+LONG_LAYER = [
+    # name, B, T, q_pos0, n_kv, cap, H, Hkv, top_k: whole-layer calls past
+    # 65536 cached tokens (indexer scores, the streamed top-k, attention)
+    ("decode_gqa_100000", 2, 1, 99999, 100000, 100032, 16, 4, 2048),
+    ("decode_mqa_262144", 1, 4, 262140, 262144, 262144, 32, 1, 2048),
+    ("prefill_chunk_70000", 1, 24, 69976, 70000, 70016, 8, 8, 2048),
+]
+
+
+@pytest.mark.parametrize("case", LONG_LAYER, ids=[c[0] for c in LONG_LAYER])
+def test_layer_past_65536_tokens(case):
+    """The whole layer on caches of 70000 to 262144 tokens, every query row
+    against the oracle: float32 indexer scores, the selection bit-exact,
+    attention outputs and log-sum-exp within tolerance."""
+    name, B, T, q_pos0, n_kv, cap, H, Hkv, k = case
+    wl = Workload(name=name, dtype="bf16", batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, idx_heads=32, idx_dim=128,
+                  top_k=k, heads=H, kv_heads=Hkv, head_dim=128, seed=zlib.crc32(name.encode()) % 1000,
+                  qidx_std=1 / math.sqrt(128), kidx_std=1.0, w_std=1 / math.sqrt(32))
+    g = make_inputs(wl, DEV, kv_capacity=cap)
+    res = _forward(g, wl, k, q_pos0, n_kv, return_lse=True)
+    sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=q_pos0, n_kv=n_kv)
+    torch.cuda.synchronize()
+    cpu = _to(g, "cpu")
+    for b in range(B):
+        _check_sequence(wl, cpu, res, sc, b, range(T))
+
+
+def test_decode_varlen_past_65536_tokens():
+    """A decode batch whose sequences run from 2 to 100000 tokens: each
+    sequence against the oracle and against the layer run on it alone."""
+    lens, T, cap, k = [100000, 66000, 30000, 3000, 2], 2, 100000, 2048
+    full = Workload(name="varlen_long", dtype="bf16", batch=len(lens), n_q=T, q_pos0=cap - T, n_kv=cap,
+                    idx_heads=32, idx_dim=128, top_k=k, heads=8, kv_heads=2, head_dim=128, seed=77,
+                    qidx_std=1 / math.sqrt(128), kidx_std=1.0, w_std=1 / math.sqrt(32))
+    g = make_inputs(full, DEV)
+    seq = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    res = dsa.forward_varlen(g["qidx"], g["w"], g["kidx"], g["q"], g["k"], g["v"], seq, top_k=k,
+                             scale=full.scale, return_mask=True, return_lse=True)
+    torch.cuda.synchronize()
+    cpu = _to(g, "cpu")
+    for b, n in enumerate(lens):
+        one = Workload(**{**full.__dict__, "batch": 1, "q_pos0": n - T, "n_kv": n})
+        sub = {key: v[b : b + 1] for key, v in cpu.items()}
+        _check_sequence(one, sub, {key: v[b : b + 1] for key, v in res.items()}, None, 0, range(T))
+        alone = dsa.forward(g["qidx"][b : b + 1], g["w"][b : b + 1], g["kidx"][b : b + 1].contiguous(),
+                            g["q"][b : b + 1], g["k"][b : b + 1].contiguous(), g["v"][b : b + 1].contiguous(),
+                            top_k=k, q_pos0=n - T, n_kv=n, scale=full.scale, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(res["indices"][b], alone["indices"][0])
+        assert torch.equal(res["out"][b], alone["out"][0])
+        assert torch.equal(res["lse"][b], alone["lse"][0])
+
+
 STREAM_SEL = [
     # name, B, T, q_pos0, top_k, recipe: forward calls with >= 512 rows and
     # rows past 16384 tokens select from survivor lists (scores not stored)
