@@ -119,10 +119,13 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[kQB], l_run[kQB];
+  // running maximum (log2 units), its negation as the exponent offset (0
+  // until the row has a kept key), and the row sum
+  float m_run[kQB], nm_run[kQB], l_run[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
     m_run[qb] = fneg_inf();
+    nm_run[qb] = 0.f;
     l_run[qb] = 0.f;
   }
 
@@ -263,7 +266,10 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
           for (int qb = 0; qb < kQB; ++qb) {
             const bool need = mx_all[qb] > m_run[qb] + kLazyMax;
             const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mx_all[qb]) : 1.f;
-            if (need) m_run[qb] = mx_all[qb];
+            if (need) {
+              m_run[qb] = mx_all[qb];
+              nm_run[qb] = -mx_all[qb];
+            }
             l_run[qb] *= alpha;
 #pragma unroll
             for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
@@ -273,7 +279,6 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
         bf16x8 pf[kQB][2];
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb) {
-          const float m_use = m_run[qb] == fneg_inf() ? 0.f : m_run[qb];
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
             bf16x8 pv;
@@ -281,7 +286,7 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                pv[4 * hf + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], sl2, -m_use));
+                pv[4 * hf + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], sl2, nm_run[qb]));
             pf[qb][ks] = pv;
             l_run[qb] = sum8_bf16(pv, l_run[qb]);
           }

@@ -572,7 +572,12 @@ def test_layer_past_65536_tokens(case):
     g = make_inputs(wl, DEV, kv_capacity=cap)
     res = _forward(g, wl, k, q_pos0, n_kv, return_lse=True)
     sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=q_pos0, n_kv=n_kv)
+    # the streamed selection's own limit is 65536 tokens: past it the call
+    # runs as dsa_forward, bit for bit
+    st = _forward(g, wl, k, q_pos0, n_kv, return_lse=True, stream_select=True)
     torch.cuda.synchronize()
+    for key in ("out", "lse", "indices"):
+        assert torch.equal(st[key], res[key]), key
     cpu = _to(g, "cpu")
     for b in range(B):
         _check_sequence(wl, cpu, res, sc, b, range(T))
