@@ -116,13 +116,28 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t spare = (uint32_t)(kSelBins + lane);  // the count word of a lane without a candidate
 
-  // Score range of the row (compare-and-select, which skips NaN and, unlike
-  // fminf, adds no canonicalising copy of every element).
+  // Score range of the row: three-operand min / max over pairs of
+  // elements, one instruction per element for both bounds (IEEE mode: a
+  // quiet NaN, the "no token" mark, loses to any number). Written as single
+  // instructions because fminf / fmaxf first canonicalise every operand.
   float lo = __uint_as_float(0x7f800000u), hi = -lo;
-  for_each([&](float v, uint32_t) {
-    lo = v < lo ? v : lo;
-    hi = v > hi ? v : hi;
-  });
+  {
+    float held = lo;
+    int n_seen = 0;  // a compile-time count once for_each is unrolled
+    for_each([&](float v, uint32_t) {
+      if (n_seen & 1) {
+        asm("v_min3_f32 %0, %1, %2, %3" : "=v"(lo) : "v"(lo), "v"(held), "v"(v));
+        asm("v_max3_f32 %0, %1, %2, %3" : "=v"(hi) : "v"(hi), "v"(held), "v"(v));
+      } else {
+        held = v;
+      }
+      ++n_seen;
+    });
+    if (n_seen & 1) {
+      asm("v_min_f32 %0, %1, %2" : "=v"(lo) : "v"(lo), "v"(held));
+      asm("v_max_f32 %0, %1, %2" : "=v"(hi) : "v"(hi), "v"(held));
+    }
+  }
   lo = __ockl_wfred_min_f32(lo);
   hi = __ockl_wfred_max_f32(hi);
   for (int i = tid; i < NBUF * (kSelBins + 64); i += NT) (&sh.hist[0][0])[i] = 0u;
