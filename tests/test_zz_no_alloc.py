@@ -23,9 +23,11 @@ def _wl(name, B, T, q_pos0, n_kv, top_k, H, Hkv, D, seed):
                     w_std=1 / math.sqrt(32))
 
 
-# decode batch (split partials in the array), a smaller decode batch, then a
-# small prefill-shaped call (score rows and mask in the array)
+# a decode batch past 65536 cached tokens (the streamed top-k), a decode
+# batch (split partials in the array), a smaller decode batch, then a small
+# prefill-shaped call (score rows and mask in the array)
 CALLS = [
+    _wl("noalloc_decode_B2_L100000", 2, 1, 99999, 100000, 2048, 16, 4, 128, 20),
     _wl("noalloc_decode_B8_L8192", 8, 1, 8191, 8192, 2048, 32, 32, 128, 21),
     _wl("noalloc_decode_B3_L1500", 3, 1, 1499, 1500, 300, 16, 16, 128, 22),
     _wl("noalloc_prefill_B2_T300", 2, 300, 100, 400, 64, 8, 8, 128, 23),
