@@ -98,6 +98,46 @@ def test_fp8_indexer_parity(case):
             assert ok, f"b{b} row {i}: selection differs beyond near-ties ({nd})"
 
 
+@pytest.mark.parametrize("case", [("decode_100000", 2, 1, 99999, 100000, 2048),
+                                  ("prefill_chunk_70000", 1, 16, 69984, 70000, 2048)],
+                         ids=["decode_100000", "prefill_chunk_70000"])
+def test_fp8_indexer_past_65536_tokens(case):
+    """The fp8 reading on caches past 65536 tokens (decode and prefill
+    kernels, the streamed top-k): codes and scales bit-exact, scores within
+    the quantised-operand bound, selections exact up to near-ties."""
+    name, B, T, p0, nkv, k = case
+    wl = Workload(name=name, dtype="bf16", batch=B, n_q=T, q_pos0=p0, n_kv=nkv, idx_heads=32, idx_dim=128,
+                  top_k=k, heads=4, kv_heads=4, head_dim=64, seed=zlib.crc32(name.encode()) % 1000,
+                  qidx_std=1 / math.sqrt(128), kidx_std=1.0, w_std=1 / math.sqrt(32))
+    g = make_inputs(wl, DEV)
+    q8, wq = dsa.quantize_fp8(g["qidx"], g["w"])
+    k8, ks = dsa.quantize_keys_fp8(g["kidx"], pos0=0, count=nkv)
+    sc = dsa.index_scores_fp8(q8, wq, k8, ks, q_pos0=p0, n_kv=nkv)
+    mask, idx = dsa.topk_mask(sc, q_pos0=p0, n_kv=nkv, top_k=k)
+    torch.cuda.synchronize()
+    sc_np, idx_np = to_np(sc), to_np(idx)
+    q8_np, k8_np = _codes(q8), _codes(k8)
+    for b in range(B):
+        qb, wb, kb = to_np(g["qidx"][b]).astype(np.float64), to_np(g["w"][b]), to_np(g["kidx"][b, :nkv]).astype(np.float64)
+        s64, oq8, owq, ok8, oks = index_scores_fp8(qb, wb, kb, p0)
+        assert np.array_equal(q8_np[b], oq8)
+        assert np.array_equal(k8_np[b, :nkv], ok8)
+        assert np.array_equal(to_np(ks[b, :nkv]), oks)
+        assert np.array_equal(to_np(wq[b]), owq)
+        s32 = round_scores_fp32(s64)
+        for i in range(T):
+            p = p0 + i
+            bound = oks[: p + 1].astype(np.float64) * score_bound(oq8[i], owq[i].astype(np.float64),
+                                                                  ok8[: p + 1], 128, 32)
+            err = np.abs(sc_np[b, i, : p + 1].astype(np.float64) - s64[i, : p + 1])
+            assert np.all(err <= bound), f"b{b} row {i}: fp8 score error {err.max()} above bound"
+            assert np.all(np.isneginf(sc_np[b, i, p + 1 :]))
+            gsel = np.array(sorted(int(x) for x in idx_np[b, i] if x >= 0))
+            osel = select_topk(s32[i], p, k)
+            ok, nd, _ = selection_ok(gsel, osel, s64[i], p, k)
+            assert ok, f"b{b} row {i}: selection differs beyond near-ties ({nd})"
+
+
 def test_fp8_indexer_prefill_L4096_sampled_rows():
     """Full-size prefill workload (the shape the bench's fp8 study runs): all
     rows scored and selected on the GPU, sampled rows checked against the

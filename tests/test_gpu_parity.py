@@ -552,11 +552,13 @@ def test_topk_rows_past_65536(case):
 
 
 LONG_LAYER = [
-    # name, B, T, q_pos0, n_kv, cap, H, Hkv, top_k: whole-layer calls past
-    # 65536 cached tokens (indexer scores, the streamed top-k, attention)
-    ("decode_gqa_100000", 2, 1, 99999, 100000, 100032, 16, 4, 2048),
-    ("decode_mqa_262144", 1, 4, 262140, 262144, 262144, 32, 1, 2048),
-    ("prefill_chunk_70000", 1, 24, 69976, 70000, 70016, 8, 8, 2048),
+    # name, dtype, B, T, q_pos0, n_kv, cap, DI, H, Hkv, D, top_k: whole-layer
+    # calls past 65536 cached tokens (indexer scores, the streamed top-k,
+    # attention)
+    ("decode_gqa_100000", "bf16", 2, 1, 99999, 100000, 100032, 128, 16, 4, 128, 2048),
+    ("decode_mqa_262144", "bf16", 1, 4, 262140, 262144, 262144, 128, 32, 1, 128, 2048),
+    ("prefill_chunk_70000", "bf16", 1, 24, 69976, 70000, 70016, 128, 8, 8, 128, 2048),
+    ("decode_fp32_70000", "fp32", 1, 3, 69997, 70000, 70000, 64, 4, 2, 64, 1000),
 ]
 
 
@@ -565,10 +567,10 @@ def test_layer_past_65536_tokens(case):
     """The whole layer on caches of 70000 to 262144 tokens, every query row
     against the oracle: float32 indexer scores, the selection bit-exact,
     attention outputs and log-sum-exp within tolerance."""
-    name, B, T, q_pos0, n_kv, cap, H, Hkv, k = case
-    wl = Workload(name=name, dtype="bf16", batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, idx_heads=32, idx_dim=128,
-                  top_k=k, heads=H, kv_heads=Hkv, head_dim=128, seed=zlib.crc32(name.encode()) % 1000,
-                  qidx_std=1 / math.sqrt(128), kidx_std=1.0, w_std=1 / math.sqrt(32))
+    name, dt, B, T, q_pos0, n_kv, cap, DI, H, Hkv, D, k = case
+    wl = Workload(name=name, dtype=dt, batch=B, n_q=T, q_pos0=q_pos0, n_kv=n_kv, idx_heads=32, idx_dim=DI,
+                  top_k=k, heads=H, kv_heads=Hkv, head_dim=D, seed=zlib.crc32(name.encode()) % 1000,
+                  qidx_std=1 / math.sqrt(DI), kidx_std=1.0, w_std=1 / math.sqrt(32))
     g = make_inputs(wl, DEV, kv_capacity=cap)
     res = _forward(g, wl, k, q_pos0, n_kv, return_lse=True)
     sc = dsa.index_scores(g["qidx"], g["w"], g["kidx"], q_pos0=q_pos0, n_kv=n_kv)
