@@ -49,6 +49,11 @@ void topk_mask_kernel(TopkParams a) {
 //  4. Otherwise (an unrepresentative sample, or heavy ties) the workgroup
 //     finds the exact threshold by radix passes that re-read the row, and a
 //     last pass writes the selection: slower, exact.
+// Rows longer than the register-resident kernel holds (65537 to 262144
+// tokens) always take a second instantiation, whatever the row count and
+// top_k: 32-bit survivor indices, a sample of up to 128 segments at the
+// smallest stride that fits (every 13th segment at 100000 tokens), and the
+// mask bitmap laid over the survivor arrays once they are in registers.
 constexpr int kLongNW = 4, kLongNT = kLongNW * 64;
 constexpr int kLongCap = 4096;               // survivors held in LDS
 constexpr int kLongEPT = 16;                 // row elements per thread per block
