@@ -404,8 +404,7 @@ dsa_status check_proj_dims(const dsa_proj_dims* d) {
 
 size_t proj_ws(const dsa_proj_dims& d) {
   const int M = d.batch * d.n_q;
-  return std::max(dsa::proj_partial_bytes(M, d.idx_heads * d.idx_dim, d.q_rank),
-                  dsa::proj_partial_bytes(M, d.idx_dim + d.idx_heads, d.hidden));
+  return dsa::proj_pair_partial_bytes(M, d.idx_heads * d.idx_dim, d.q_rank, d.idx_dim + d.idx_heads, d.hidden);
 }
 
 }  // namespace
@@ -507,7 +506,6 @@ dsa_status dsa_indexer_project(const dsa_proj_dims* dims, const void* x, const v
   q.mode = 0;
   q.out_bf16 = qidx;
   q.partial = need > 0 ? static_cast<float*>(ws) : nullptr;
-  DSA_TRY(hip_status(dsa::launch_proj(q, ws_bytes, st), "q_b projection launch", st));
   dsa::ProjParams k{};
   k.x = x;
   k.w0 = w_k;
@@ -523,7 +521,7 @@ dsa_status dsa_indexer_project(const dsa_proj_dims* dims, const void* x, const v
   k.q_pos0 = d.q_pos0;
   k.kv_cap = d.kv_capacity;
   k.partial = need > 0 ? static_cast<float*>(ws) : nullptr;
-  DSA_TRY(hip_status(dsa::launch_proj(k, ws_bytes, st), "k / projection launch", st));
+  DSA_TRY(hip_status(dsa::launch_proj_pair(q, k, ws_bytes, st), "front-end projection launch", st));
   return ok();
 }
 

@@ -70,6 +70,11 @@ struct ProjParams {
 // product (0: no split).
 size_t proj_partial_bytes(int M, int N, int K);
 hipError_t launch_proj(const ProjParams& p, size_t ws_bytes, hipStream_t st);
+// Both front-end products of one call (q_b, and k with projection), their
+// launches arranged together where that saves launches; the workspace must
+// hold proj_pair_partial_bytes (both products' partials share p.partial).
+hipError_t launch_proj_pair(const ProjParams& q, const ProjParams& k, size_t ws_bytes, hipStream_t st);
+size_t proj_pair_partial_bytes(int M, int Nq, int Kq, int Nk, int Kk);
 
 // Top-k -> bitmask (+ ascending indices).
 struct TopkParams {

@@ -23,7 +23,11 @@
 //
 // Thin products (few tokens, or only D_I + H_I outputs) split K over
 // blockIdx.z into float32 partials, which proj_reduce_kernel sums in split
-// order (deterministic) before the same epilogue.
+// order (deterministic) before the same epilogue. Calls of at most 64 tokens
+// run both products' tiles in one launch and both products' sums in a
+// second.
+#include <algorithm>
+
 #include "dsa_device.hpp"
 #include "dsa_kernels.hpp"
 
@@ -75,6 +79,20 @@ __device__ __forceinline__ void store_out(const ProjParams& a, int m, int n, f32
 // s_waitcnt immediate that waits until at most n vector-memory loads are
 // outstanding (expcnt and lgkmcnt left unconstrained).
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// Waits until at most `newer` stages of PS loads each are outstanding
+// (newer <= N; the immediate has to be a constant, hence one case each).
+template <int PS, int N>
+__device__ __forceinline__ void wait_stages(int newer) {
+  if constexpr (N > 0) {
+    if (newer >= N) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(N * PS));
+      return;
+    }
+    wait_stages<PS, N - 1>(newer);
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+}
 
 // Tile of workgroup `bid` in a 1-D grid of 8 * per_xcd: workgroups are
 // dealt to the 8 XCDs round-robin (bid % 8), so each XCD gets one contiguous
@@ -115,10 +133,39 @@ using ThinShape = ProjShape<2, 2, 4, 1, 3>;
 // projection product (D_I + H_I <= 160) in one tile; one workgroup per CU
 // with three stages in flight, as these run one wave of workgroups deep
 using AllOutShape = ProjShape<4, 1, 2, 10, 4>;
+// Calls of at most 64 tokens (decode): 64 tokens x 64 outputs, 4 waves of
+// 32 x 32, three stages (48 KiB of LDS, three workgroups per CU). Every
+// workgroup reads the whole token tile for its K range, so the tile is made
+// wide and K split instead (q_b: 64 output tiles x 4 splits read a quarter
+// of the activation bytes that 256 tiles of 16 outputs do).
+using FewShape = ProjShape<2, 2, 2, 2, 3>;
+constexpr int kFewMaxM = FewShape::BM;
 
+// One product's tiles in a launch.
+struct ProjTask {
+  ProjParams p;
+  int m_tiles, n_tiles, n_split, per_xcd;  // workgroups 8 * per_xcd (0: no task)
+};
+
+// Sums the K-split partials of four outputs (quad i of the product) in
+// split order.
+__device__ __forceinline__ void reduce_quad(const ProjParams& a, int n_split, int Npad, long long i) {
+  const int quads = Npad / 4;
+  if (i >= (long long)a.M * quads) return;
+  const int m = (int)(i / quads), n = (int)(i % quads) * 4;
+  if (n >= a.N0 + a.N1) return;
+  const float* src = a.partial + (size_t)m * Npad + n;
+  const size_t zstride = (size_t)a.M * Npad;
+  f32x4 s = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll 8
+  for (int z = 1; z < n_split; ++z) s += *reinterpret_cast<const f32x4*>(src + z * zstride);
+  store_out(a, m, n, s);
+}
+
+// Tile `bid` of one product.
 template <class S>
-__global__ __launch_bounds__(64 * S::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
-void proj_gemm_kernel(ProjParams a, int m_tiles, int n_tiles, int n_split, int per_xcd) {
+__device__ __forceinline__ void proj_tile(const ProjParams& a, int m_tiles, int n_tiles, int n_split, int per_xcd,
+                                          int bid) {
   constexpr int MB = S::MB, NB = S::NB, BM = S::BM, BN = S::BN, STAGES = S::STAGES;
   constexpr int A_BYTES = BM * kRowB;      // token tile
   constexpr int STAGE = A_BYTES + BN * kRowB;
@@ -129,7 +176,7 @@ void proj_gemm_kernel(ProjParams a, int m_tiles, int n_tiles, int n_split, int p
   __shared__ __attribute__((aligned(16))) unsigned char lds[STAGES * STAGE];
 
   int mt, nt, z;
-  if (!tile_of(blockIdx.x, m_tiles, n_tiles, n_split, per_xcd, mt, nt, z)) return;  // whole workgroup
+  if (!tile_of(bid, m_tiles, n_tiles, n_split, per_xcd, mt, nt, z)) return;  // whole workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, c = lane & 15, g = lane >> 4;
   const int wm = wave / S::WGN, wn = wave % S::WGN;
   const int n0 = nt * BN, m0 = mt * BM;
@@ -179,9 +226,8 @@ void proj_gemm_kernel(ProjParams a, int m_tiles, int n_tiles, int n_split, int p
     // stage kt has landed once at most the loads of the stages issued after
     // it (min(STAGES - 2, nk - 1 - kt) of them) are still outstanding
     const int newer = min(STAGES - 2, nk - 1 - kt);
-    if (STAGES >= 4 && newer >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STAGE));
-    else if (STAGES >= 3 && newer == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STAGE));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    static_assert((STAGES - 2) * PER_STAGE <= 63, "outstanding loads fit the counter");
+    wait_stages<PER_STAGE, STAGES - 2>(newer);
     // every wave's share of stage kt is visible, and every wave is done with
     // the buffer the next load overwrites (it held stage kt - 1)
     asm volatile("" ::: "memory");
@@ -222,19 +268,25 @@ void proj_gemm_kernel(ProjParams a, int m_tiles, int n_tiles, int n_split, int p
   }
 }
 
-// Sums the K-split partials of four outputs per thread, in split order.
-__global__ __launch_bounds__(256) void proj_reduce_kernel(ProjParams a, int n_split, int Npad) {
-  const int quads = Npad / 4;
+// The tiles of task t0, then (kTwo) those of task t1, in one launch.
+template <class S, bool kTwo>
+__global__ __launch_bounds__(64 * S::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+void proj_gemm_kernel(ProjTask t0, ProjTask t1) {
+  const int bid = (int)blockIdx.x;
+  if (!kTwo || bid < 8 * t0.per_xcd) {
+    proj_tile<S>(t0.p, t0.m_tiles, t0.n_tiles, t0.n_split, t0.per_xcd, bid);
+    return;
+  }
+  if constexpr (kTwo) proj_tile<S>(t1.p, t1.m_tiles, t1.n_tiles, t1.n_split, t1.per_xcd, bid - 8 * t0.per_xcd);
+}
+
+// Sums the K-split partials of four outputs per thread, in split order:
+// quads of product a first, then those of product b (nb_quads = 0: none).
+__global__ __launch_bounds__(256) void proj_reduce_kernel(ProjParams a, int n_split, int Npad, ProjParams b,
+                                                          int b_split, int b_Npad, long long a_threads) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (long long)a.M * quads) return;
-  const int m = (int)(i / quads), n = (int)(i % quads) * 4;
-  if (n >= a.N0 + a.N1) return;
-  const float* src = a.partial + (size_t)m * Npad + n;
-  const size_t zstride = (size_t)a.M * Npad;
-  f32x4 s = *reinterpret_cast<const f32x4*>(src);
-#pragma unroll 8
-  for (int z = 1; z < n_split; ++z) s += *reinterpret_cast<const f32x4*>(src + z * zstride);
-  store_out(a, m, n, s);
+  if (i < a_threads) reduce_quad(a, n_split, Npad, i);
+  else reduce_quad(b, b_split, b_Npad, i - a_threads);
 }
 
 // Splits of K (a divisor of K / 64) so that the grid has at least `target`
@@ -254,7 +306,7 @@ int choose_split(long long tiles, int K, int target) {
 
 // How one product is run: tile shape, tile counts and K splits. The same
 // plan sizes the workspace and drives the launch.
-enum ShapeId { kWide, kAllOut, kThin };
+enum ShapeId { kWide, kAllOut, kThin, kFew };
 struct Plan {
   ShapeId shape;
   int BM, BN;
@@ -268,6 +320,8 @@ Plan make_plan(ShapeId id, int M, int N, int K, int split_target) {
   return pl;
 }
 Plan plan_for(int M, int N, int K) {
+  // at most 64 tokens: one token tile, K split to fill the chip
+  if (M <= kFewMaxM) return make_plan<FewShape>(kFew, M, N, K, 256);
   // many tokens, wide output (q_b): square tiles, no split
   if (M >= 1024 && N % WideShape::BN == 0) return make_plan<WideShape>(kWide, M, N, K, 0);
   // many tokens, narrow output (k and projection): one tile spans every
@@ -277,33 +331,55 @@ Plan plan_for(int M, int N, int K) {
   return make_plan<ThinShape>(kThin, M, N, K, 512);
 }
 
-template <class S>
-hipError_t launch_plan(ProjParams p, const Plan& pl, size_t ws_bytes, hipStream_t st) {
+// The task of a product under plan pl, its partials (when split) at
+// p.partial, which must hold partial_bytes(pl, M).
+size_t partial_bytes(const Plan& pl, int M) { return pl.split > 1 ? (size_t)pl.split * M * pl.n_tiles * pl.BN * 4 : 0; }
+hipError_t make_task(ProjParams p, const Plan& pl, size_t avail, ProjTask& t) {
   if (pl.m_tiles > 65535) return hipErrorInvalidValue;
-  const int Npad = (int)pl.n_tiles * S::BN;
-  if (pl.split > 1 && (!p.partial || (size_t)pl.split * p.M * Npad * 4 > ws_bytes)) return hipErrorInvalidValue;
+  if (pl.split > 1 && (!p.partial || partial_bytes(pl, p.M) > avail)) return hipErrorInvalidValue;
   if (pl.split == 1) p.partial = nullptr;
   p.k_split = p.K / pl.split;
   const long long total = pl.n_tiles * pl.m_tiles * pl.split;
   const long long per_xcd = (total + 7) / 8;
-  if (8 * per_xcd > 0x7fffffffll) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((proj_gemm_kernel<S>), dim3((unsigned)(8 * per_xcd)), dim3(64 * S::WAVES), 0, st, p,
-                     (int)pl.m_tiles, (int)pl.n_tiles, pl.split, (int)per_xcd);
-  if (pl.split > 1) {
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const long long threads = (long long)p.M * (Npad / 4);
-    hipLaunchKernelGGL(proj_reduce_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, p, pl.split,
-                       Npad);
-  }
+  if (8 * per_xcd > 0x3fffffffll) return hipErrorInvalidValue;
+  t = ProjTask{p, (int)pl.m_tiles, (int)pl.n_tiles, pl.split, (int)per_xcd};
+  return hipSuccess;
+}
+// Sums of the split tasks among t0 and t1 (t1.per_xcd = 0: no second task).
+hipError_t launch_reduce(const ProjTask& t0, const Plan& p0, const ProjTask& t1, const Plan& p1, hipStream_t st) {
+  const bool r0 = p0.split > 1, r1 = t1.per_xcd > 0 && p1.split > 1;
+  if (!r0 && !r1) return hipSuccess;
+  const ProjParams none{};
+  const ProjParams& a = r0 ? t0.p : t1.p;
+  const Plan& pa = r0 ? p0 : p1;
+  const ProjParams& b = r0 && r1 ? t1.p : none;
+  const long long a_threads = (long long)a.M * (pa.n_tiles * pa.BN / 4);
+  const long long b_threads = r0 && r1 ? (long long)b.M * (p1.n_tiles * p1.BN / 4) : 0;
+  const long long blocks = (a_threads + b_threads + 255) / 256;
+  hipLaunchKernelGGL(proj_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, pa.split,
+                     (int)(pa.n_tiles * pa.BN), b, p1.split, (int)(p1.n_tiles * p1.BN), a_threads);
   return hipGetLastError();
+}
+template <class S>
+hipError_t launch_plan(const ProjParams& p, const Plan& pl, size_t ws_bytes, hipStream_t st) {
+  ProjTask t{};
+  hipError_t e = make_task(p, pl, ws_bytes, t);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((proj_gemm_kernel<S, false>), dim3((unsigned)(8 * t.per_xcd)), dim3(64 * S::WAVES), 0, st, t,
+                     ProjTask{});
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce(t, pl, ProjTask{}, pl, st);
 }
 
 }  // namespace
 
-size_t proj_partial_bytes(int M, int N, int K) {
-  const Plan pl = plan_for(M, N, K);
-  return pl.split > 1 ? (size_t)pl.split * M * pl.n_tiles * pl.BN * 4 : 0;
+size_t proj_partial_bytes(int M, int N, int K) { return partial_bytes(plan_for(M, N, K), M); }
+
+size_t proj_pair_partial_bytes(int M, int Nq, int Kq, int Nk, int Kk) {
+  const size_t bq = proj_partial_bytes(M, Nq, Kq), bk = proj_partial_bytes(M, Nk, Kk);
+  if (M <= kFewMaxM) return (bq + 255) / 256 * 256 + bk;  // both products' partials at once
+  return std::max(bq, bk);
 }
 
 hipError_t launch_proj(const ProjParams& p, size_t ws_bytes, hipStream_t st) {
@@ -312,8 +388,37 @@ hipError_t launch_proj(const ProjParams& p, size_t ws_bytes, hipStream_t st) {
   switch (pl.shape) {
     case kWide: return launch_plan<WideShape>(p, pl, ws_bytes, st);
     case kAllOut: return launch_plan<AllOutShape>(p, pl, ws_bytes, st);
+    case kFew: return launch_plan<FewShape>(p, pl, ws_bytes, st);
     default: return launch_plan<ThinShape>(p, pl, ws_bytes, st);
   }
+}
+
+hipError_t launch_proj_pair(const ProjParams& q, const ProjParams& k, size_t ws_bytes, hipStream_t st) {
+  if (q.K % kBK != 0 || k.K % kBK != 0 || q.M < 1 || q.M != k.M || q.N0 % 4 != 0 || k.N0 % 4 != 0)
+    return hipErrorInvalidValue;
+  if (q.M > kFewMaxM) {  // one product after the other, sharing the workspace
+    hipError_t e = launch_proj(q, ws_bytes, st);
+    if (e != hipSuccess) return e;
+    return launch_proj(k, ws_bytes, st);
+  }
+  // Few tokens: both products' tiles in one launch, their partials side by
+  // side in the workspace, both sums in a second launch.
+  const Plan pq = plan_for(q.M, q.N0 + q.N1, q.K), pk = plan_for(k.M, k.N0 + k.N1, k.K);
+  const size_t bq = (partial_bytes(pq, q.M) + 255) / 256 * 256;
+  if (bq > ws_bytes) return hipErrorInvalidValue;
+  ProjParams kk = k;
+  if (k.partial) kk.partial = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(k.partial) + bq);
+  ProjTask tq{}, tk{};
+  hipError_t e = make_task(q, pq, ws_bytes, tq);
+  if (e != hipSuccess) return e;
+  e = make_task(kk, pk, ws_bytes - bq, tk);
+  if (e != hipSuccess) return e;
+  const long long blocks = 8ll * tq.per_xcd + 8ll * tk.per_xcd;
+  hipLaunchKernelGGL((proj_gemm_kernel<FewShape, true>), dim3((unsigned)blocks), dim3(64 * FewShape::WAVES), 0, st,
+                     tq, tk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce(tq, pq, tk, pk, st);
 }
 
 }  // namespace dsa
