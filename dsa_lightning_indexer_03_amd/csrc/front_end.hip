@@ -281,7 +281,8 @@ void proj_gemm_kernel(ProjTask t0, ProjTask t1) {
 }
 
 // Sums the K-split partials of four outputs per thread, in split order:
-// quads of product a first, then those of product b (nb_quads = 0: none).
+// the a_threads quads of product a first, then those of product b (b.M = 0:
+// none).
 __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjParams a, int n_split, int Npad, ProjParams b,
                                                           int b_split, int b_Npad, long long a_threads) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
