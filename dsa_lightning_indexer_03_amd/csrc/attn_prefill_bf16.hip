@@ -210,7 +210,9 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
         full = full && (lo & hi) == 0xffffffffu;
       }
       if (ballot64(any) != 0ull) {
-        // S^T = K Q^T
+        // S^T = K Q^T (the scheduler's small-GEMM strategy interleaves the K
+        // fragment reads with the MFMAs; measured 2-3% faster per call)
+        __builtin_amdgcn_iglp_opt(0);
         f32x4 sacc[4][kQB];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -291,7 +293,8 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
             l_run[qb] = sum8_bf16(pv, l_run[qb]);
           }
         }
-        // O^T += V^T P^T
+        // O^T += V^T P^T (same strategy)
+        __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
