@@ -233,6 +233,9 @@ __device__ __forceinline__ void proj_tile(const ProjParams& a, int m_tiles, int 
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     if (kt + STAGES - 1 < nk) dload(kt + STAGES - 1);
+    // the scheduler's small-GEMM strategy interleaves the fragment reads
+    // with the MFMAs (6% faster on the 4096-token call)
+    __builtin_amdgcn_iglp_opt(0);
     const unsigned char* sa = lds + (kt % STAGES) * STAGE;
     const unsigned char* sb = sa + A_BYTES;
 #pragma unroll
