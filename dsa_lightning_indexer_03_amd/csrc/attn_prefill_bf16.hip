@@ -36,12 +36,19 @@
 // four consecutive keys.
 //
 // Softmax. Scores are masked with one sign-extending bit extract and one
-// bitfield insert per element, exponentiated with exp2 against a running
-// maximum that is only raised (and O rescaled) when a tile's maximum exceeds
-// it by more than 2^8; until then probabilities stay <= 256, which float32
-// sums and bf16 P carry without loss. The row sum is taken over the bf16
-// probabilities that enter P V (two per dot2 instruction), and the final
-// normalisation divides by it, so the result is softmax over the kept keys.
+// bitfield insert per element and exponentiated with exp2 against a per-row
+// offset. The offset is the exact maximum of the row's first tile with a
+// kept key; later tiles take no maximum at all. A lane's share of a tile's
+// row sum bounds every probability in it, so when no share exceeds 2^40 the
+// tile is accepted as computed; otherwise (scores that rose by about 36 log2
+// units or more) the tile's exact maxima are taken, the offset raised, O and
+// the sums rescaled, and the probabilities computed again. Probabilities thus
+// stay <= 2^40 (float32 sums and bf16 P carry them without loss, and O stays
+// finite for |v| < 2^70), and since the offset never exceeds the row's true
+// maximum the largest probability is >= 1, so nothing that matters
+// underflows. The row sum is taken over the bf16 probabilities that enter
+// P V (two per dot2 instruction), and the final normalisation divides by it,
+// so the result is softmax over the kept keys.
 //
 // Scheduling. Workgroup ids are mapped so that all query tiles of one
 // (sequence, head) pair land on the same XCD (id mod 8), sharing its L2 for
@@ -56,8 +63,7 @@ namespace {
 using namespace attn_bf16;
 
 constexpr int kStage = 2 * kTileBytes;       // K tile then V tile
-
-
+constexpr float kSumCap = 1099511627776.0f;  // 2^40: largest accepted lane share of a tile's row sum
 constexpr int kQB = 2;               // 16-query blocks per wave
 constexpr int kQW = 16 * kQB;        // queries per wave
 #ifndef DSA_ATTN_WAVES
@@ -119,8 +125,8 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
     for (int qb = 0; qb < kQB; ++qb) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running maximum (log2 units), its negation as the exponent offset (0
-  // until the row has a kept key), and the row sum
+  // exponent offset (log2 units; -inf until the row has a kept key), its
+  // negation (0 until then), and the row sum
   float m_run[kQB], nm_run[kQB], l_run[kQB];
 #pragma unroll
   for (int qb = 0; qb < kQB; ++qb) {
@@ -227,11 +233,57 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
             for (int qb = 0; qb < kQB; ++qb) sacc[kb][qb] = mma_kstep(kf, qreg[qb][kk], sacc[kb][qb]);
           }
         }
-        // Masked maxima (no masking when every query of the wave keeps the
-        // whole tile); the running maximum is raised lazily.
+        // Unkept keys to -inf (no masking when every query of the wave keeps
+        // the whole tile).
         const bool plain = ballot64(!full) == 0ull;
-        float mx_all[kQB];
-        if (plain) {
+        if (!plain) {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) {
+            const uint32_t wlo = mw[qb].x >> (4 * g), whi = mw[qb].y >> (4 * g);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                sacc[kb][qb][r] = mask_elem(sacc[kb][qb][r], kb < 2 ? wlo : whi, 16 * (kb & 1) + r);
+          }
+        }
+        // P^T in bf16 against the current exponent offset, in the accumulator
+        // layout; lt = this lane's share of the tile's row sums.
+        bf16x8 pf[kQB][2];
+        float lt[kQB];
+        auto probs = [&]() {
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) {
+            lt[qb] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+              bf16x8 pv;
+#pragma unroll
+              for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  pv[4 * hf + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], sl2, nm_run[qb]));
+              pf[qb][ks] = pv;
+              lt[qb] = sum8_bf16(pv, lt[qb]);
+            }
+          }
+        };
+        // The offset of a row is set to the exact maximum of its first tile
+        // with a kept key and raised only when a lane's share of a tile's sum
+        // exceeds 2^40 (then every probability so far is <= 2^40).
+        bool first = false;
+#pragma unroll
+        for (int qb = 0; qb < kQB; ++qb) first = first || (m_run[qb] == fneg_inf() && (mw[qb].x | mw[qb].y) != 0u);
+        bool exact = ballot64(first) != 0ull;
+        if (!exact) {
+          probs();
+          bool over = false;
+#pragma unroll
+          for (int qb = 0; qb < kQB; ++qb) over = over || lt[qb] > kSumCap;
+          exact = ballot64(over) != 0ull;
+        }
+        if (exact) {
+          float mx_all[kQB];
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) {
             float mx = fneg_inf();
@@ -239,31 +291,8 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
               for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[kb][qb][r]);
-            mx_all[qb] = mx;
+            mx_all[qb] = rows4_max(mx) * sl2;
           }
-        } else {
-#pragma unroll
-          for (int qb = 0; qb < kQB; ++qb) {
-            const uint32_t wlo = mw[qb].x >> (4 * g), whi = mw[qb].y >> (4 * g);
-            float mx = fneg_inf();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                const float v = mask_elem(sacc[kb][qb][r], kb < 2 ? wlo : whi, 16 * (kb & 1) + r);
-                sacc[kb][qb][r] = v;
-                mx = fmaxf(mx, v);
-              }
-            mx_all[qb] = mx;
-          }
-        }
-        bool need_any = false;
-#pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-          mx_all[qb] = rows4_max(mx_all[qb]) * sl2;
-          need_any = need_any || mx_all[qb] > m_run[qb] + kLazyMax;
-        }
-        if (ballot64(need_any) != 0ull) {
 #pragma unroll
           for (int qb = 0; qb < kQB; ++qb) {
             const bool need = mx_all[qb] > m_run[qb] + kLazyMax;
@@ -276,23 +305,10 @@ void attn_prefill_bf16_kernel(AttnParams a, int n_qtiles, int pairs_per_xcd) {
 #pragma unroll
             for (int db = 0; db < kDB; ++db) o[db][qb] *= alpha;
           }
+          probs();
         }
-        // P^T in bf16, in the accumulator layout; row sums over the bf16 values.
-        bf16x8 pf[kQB][2];
 #pragma unroll
-        for (int qb = 0; qb < kQB; ++qb) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            bf16x8 pv;
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                pv[4 * hf + r] = (bf16)__builtin_amdgcn_exp2f(fmaf(sacc[2 * ks + hf][qb][r], sl2, nm_run[qb]));
-            pf[qb][ks] = pv;
-            l_run[qb] = sum8_bf16(pv, l_run[qb]);
-          }
-        }
+        for (int qb = 0; qb < kQB; ++qb) l_run[qb] += lt[qb];
         // O^T += V^T P^T (same strategy)
         __builtin_amdgcn_iglp_opt(0);
 #pragma unroll

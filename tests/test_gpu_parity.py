@@ -755,6 +755,62 @@ def test_sparse_attention_arbitrary_masks(T, q_pos0, n_kv, H, Hkv, D, dt):
                 assert np.allclose(lse[b, i], ls, rtol=1e-4, atol=LSE_ATOL[dt])
 
 
+def _score_level(recipe, n_kv):
+    """Per-key level a_s: with q = 8 e + noise and k_s = a_s e + noise (e a
+    unit vector) the scaled score of key s is about 1.02 a_s in log2 units."""
+    s = np.arange(n_kv)
+    if recipe == "jumps":  # +30, then +60, then +160 above the first tile, then far below
+        return np.select([s < 64, s < 128, s < 192, s < 200], [0.0, 30.0, 90.0, 250.0], -50.0)
+    if recipe == "negative":  # every score near -150: no offset of 0 survives exp2
+        return np.full(n_kv, -150.0)
+    if recipe == "ramp":  # about +45 per 64-key tile
+        return 0.7 * s
+    raise ValueError(recipe)
+
+
+@pytest.mark.parametrize("recipe", ["jumps", "negative", "ramp"])
+@pytest.mark.parametrize("T,H,Hkv,dt", [(100, 4, 2, "bf16"), (40, 16, 1, "bf16"), (3, 8, 8, "bf16"),
+                                        (37, 4, 4, "fp32")])
+def test_sparse_attention_wide_score_range(recipe, T, H, Hkv, dt):
+    """Scores that rise by tens to hundreds of log2 units from one key tile
+    to the next, or sit far below zero: the softmax's exponent offset must
+    follow them without overflow or underflow (masked-dense, kept-list and
+    gather kernels, random masks of about half density)."""
+    D, n_kv = 128, 300
+    q_pos0 = n_kv - T
+    seed = zlib.crc32(f"{recipe}-{T}-{H}".encode())
+    rng = np.random.default_rng(seed)
+    gen = torch.Generator().manual_seed(seed)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    e = torch.randn(D, generator=gen, dtype=torch.float64)
+    e /= e.norm()
+    q = 8.0 * e + 0.3 * torch.randn(2, T, H, D, generator=gen, dtype=torch.float64)
+    lev = torch.from_numpy(_score_level(recipe, n_kv))[None, :, None, None]
+    k = lev * e + 0.3 * torch.randn(2, n_kv, Hkv, D, generator=gen, dtype=torch.float64)
+    v = torch.randn(2, n_kv, Hkv, D, generator=gen, dtype=torch.float64)
+    q, k, v = q.to(tdt), k.to(tdt), v.to(tdt)
+    L = dsa.lpad(n_kv)
+    bits = rng.random((2, T, L)) < 0.5
+    bits[:, :, n_kv:] = False
+    weights = np.uint64(1) << np.arange(32, dtype=np.uint64)
+    words = (bits.reshape(2, T, L // 32, 32).astype(np.uint64) * weights).sum(-1).astype(np.uint32)
+    mask = torch.from_numpy(words.view(np.int32)).to(DEV)
+    scale = 1 / math.sqrt(D)
+    _say(f"wide score range {recipe} T={T} H={H} Hkv={Hkv} {dt}")
+    out, lse = dsa.sparse_attention(q.to(DEV), k.to(DEV), v.to(DEV), mask, q_pos0=q_pos0, n_kv=n_kv,
+                                    scale=scale, lse=True)
+    torch.cuda.synchronize()
+    out, lse = to_np(out), to_np(lse)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    from oracle import attend_selected
+    for b in range(2):
+        for i in range(T):
+            sel = np.nonzero(bits[b, i, : q_pos0 + i + 1])[0]
+            O, ls = attend_selected(_np64(q[b, i]), _np64(k[b]), _np64(v[b]), sel, scale)
+            assert np.abs(out[b, i] - O).max() <= OUT_TOL[dt], (recipe, b, i)
+            assert np.allclose(lse[b, i], ls, rtol=1e-4, atol=LSE_ATOL[dt]), (recipe, b, i)
+
+
 def test_decode_row_equals_last_prefill_row_and_determinism():
     wl = WORKLOADS["prefill_bf16_L4096"]
     g = make_inputs(wl, DEV)
