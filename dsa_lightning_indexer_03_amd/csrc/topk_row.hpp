@@ -40,7 +40,7 @@ template <int NW, int NBUF> struct SelectShared {
   // The 64 words past the bins take the counts of lanes without a
   // candidate (one word per lane, never read), which keeps the counting
   // branch-free.
-  uint32_t hist[NBUF][kSelBins + 64];
+  alignas(16) uint32_t hist[NBUF][kSelBins + 64];
   uint32_t red[NW];               // scan partials
   float vmm[2][NW];               // per-wave min / max score
   uint32_t found[3];              // threshold bin, tokens in bins above it, tokens in it
@@ -116,6 +116,14 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t spare = (uint32_t)(kSelBins + lane);  // the count word of a lane without a candidate
 
+  // Both histograms are cleared first (16-byte stores), while the caller's
+  // loads of the scores may still be in flight.
+  {
+    constexpr int kWords = NBUF * (kSelBins + 64);
+    static_assert(kWords % 4 == 0, "whole 16-byte stores");
+    uint4* hz = reinterpret_cast<uint4*>(&sh.hist[0][0]);
+    for (int i = tid; i < kWords / 4; i += NT) hz[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   // Score range of the row: three-operand min / max over pairs of
   // elements, one instruction per element for both bounds (IEEE mode: a
   // quiet NaN, the "no token" mark, loses to any number). Written as single
@@ -140,7 +148,6 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
   }
   lo = __ockl_wfred_min_f32(lo);
   hi = __ockl_wfred_max_f32(hi);
-  for (int i = tid; i < NBUF * (kSelBins + 64); i += NT) (&sh.hist[0][0])[i] = 0u;
   if (tid == 0) sh.ncand = 0u;
   if (lane == 0) {
     sh.vmm[0][wave] = lo;
@@ -154,14 +161,17 @@ __device__ __forceinline__ KthResult select_kth(ForEach for_each, uint32_t rank,
   }
   lo = uniform_f32(lo);
   hi = uniform_f32(hi);
-  // Bin of a score: linear over [min, max]. Rounded subtraction and
-  // multiplication by a positive factor never reverse an order, so the bins
-  // are ordered like the scores. A range that is empty or overflows gives a
-  // factor of inf or 0 and the products NaN or 0 (clamped and converted to
-  // bin 0), or inf (bin 2047): still ordered, and the exact passes decide.
+  // Bin of a score: linear over [min, max], v * scale - lo * scale as one
+  // fused multiply-add, clamped to [0, 2047] by a median of three and
+  // truncated. A rounded fma with a positive factor never reverses an order,
+  // so the bins are ordered like the scores. A range that is empty or
+  // overflows gives a factor of inf or 0 and the results NaN or 0 (the
+  // median takes NaN to 0) or inf (bin 2047): still ordered, and the exact
+  // passes decide.
   const float scale = (float)kSelBins / (hi - lo);
-  auto bin_of = [lo, scale](float v) -> uint32_t {
-    return (uint32_t)fminf(fmaxf((v - lo) * scale, 0.0f), (float)(kSelBins - 1));
+  const float offset = -lo * scale;
+  auto bin_of = [offset, scale](float v) -> uint32_t {
+    return (uint32_t)__builtin_amdgcn_fmed3f(fmaf(v, scale, offset), 0.0f, (float)(kSelBins - 1));
   };
   // Each pass folds its own opaque zero into the scores, so the compiler
   // recomputes bins and keys where they are needed instead of keeping values
