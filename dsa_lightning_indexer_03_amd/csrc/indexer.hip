@@ -455,10 +455,12 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
       }
     }
   };
-  // tile of u0 landed (the S-2 later tiles may still be in flight; the query
-  // loads issued after them are then mostly done too, and the first scores
-  // wait for the rest)
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm((S - 2) * NLD));
+  // Every prologue load landed: the query fragments (issued last) and so the
+  // tiles before them. With no fragment load outstanding when the unit loop
+  // starts, its matrix instructions wait for LDS only; a fragment load left
+  // in flight would make the compiler wait for every load in flight (the
+  // tile prefetches included) in front of every unit's matrix work.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -466,7 +468,10 @@ __global__ __launch_bounds__(64 * kIdxWaves) void indexer_prefill_kernel(Indexer
   int slot = 0;
   for (long long u = u0; u < u1; ++u) {
     const int qt = um.qt_at(qp);
-    if (b != cur_b || qt != cur_qt) switch_tile(b, qt);
+    if (b != cur_b || qt != cur_qt) {
+      switch_tile(b, qt);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the new fragments, once (see the prologue)
+    }
     // stores of unit u-1, then the tile of unit u+S-1 (or the range's last
     // one again) into the slot read at unit u-1: the newest S-2 tile loads
     // are then the last operations issued when tile u+1 is waited for
